@@ -1,0 +1,178 @@
+/*
+ * rlk_logprob.h — C ABI of the strict-path selected-token logprob on MI355X (gfx950).
+ *
+ * The library computes, for every row t of a hidden-state matrix h[T,H] and its target token y_t,
+ *
+ *     z[t,v]  = sum_k h[t,k] * W[v,k]                      (the LM-head projection, W is [V,H])
+ *     z'      = z * inv_temperature
+ *     lse[t]  = log sum_v exp(z'[t,v])
+ *     logp[t] = z'[t,y_t] - lse[t]
+ *     entropy[t] = lse[t] - sum_v softmax(z')[t,v] * z'[t,v]          (optional)
+ *
+ * under one fixed numeric contract, so that each row's outputs are bitwise identical however the
+ * rows are laid out: one packed training batch, ragged rollout batches, row chunks of any size,
+ * or the vocabulary split into contiguous shards whose partial results are merged.
+ *
+ * Sources (pages about RL-Kernel, vime and vLLM on ROCm):
+ *  - RL-Kernel v0.1.0 summary (agentlenshq.com), section "Numeric execution contract": a forward
+ *    fixes its inputs, how a reduction is split, the merge order of partial results, precisions,
+ *    rounding points and math primitives. Same page, strict-path boundary table, row "Linear
+ *    logprob": actual vocab range, target ownership, local reduction, cross-rank LSE merge. Same
+ *    page, ROCm fixes list: deterministic MFMA GEMM; vocab reduction and the cross-TP vocab merge.
+ *  - nxbn.cn blog on bitwise train/rollout consistency, §3.1 (the logprob is log_softmax at the
+ *    token; its max and sum reductions decide the last bits), §3.2 (a fixed reduction tree with
+ *    fp32 intermediates; wave64 shuffle steps in a fixed order), §3.3 (the rollout recomputes the
+ *    logprob from hidden states and tokens), §3.4 (no FMA contraction; 256-byte alignment).
+ *  - kongchang.com article on bit-for-bit logprob alignment, "four key links": reduction order,
+ *    intermediate precision, rounding points, math primitives.
+ * The numeric contract itself (tile width, merge trees, primitives) is spelled out at
+ * rlk_logprob_contract_id() and in the library's kernel source.
+ *
+ * Conventions for every entry point:
+ *  - Device pointers are HIP device memory owned by the caller; the library never frees them.
+ *    Host pointers are marked "host". Every device pointer must be 16-byte aligned; a misaligned
+ *    pointer returns RLK_ERR_ALIGNMENT (there is no second code path for it).
+ *  - Matrices are row-major with unit stride along the hidden dimension (row stride = H).
+ *    hidden and W are bfloat16 bit patterns (2 bytes each); rms_gamma is bfloat16 [H].
+ *  - targets are int32 [T]; a negative target marks a padded row: its logp, lse and entropy are
+ *    written as +0.0. A target >= V writes NaN for that row and sets RLK_DEVICE_STATUS_BAD_TARGET
+ *    in the workspace status word (see rlk_logprob_device_status).
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream of the handle's device)
+ *    and runs asynchronously; forward, partials and merge neither allocate nor synchronize.
+ *  - No exception crosses the ABI. On failure nothing is enqueued, the status says why, and
+ *    rlk_last_error() holds a message (thread-local, valid until the next call on the thread).
+ *  - A handle is immutable after creation and may be used from several threads; calls that
+ *    share a workspace must be ordered by the caller (same stream or events).
+ */
+#ifndef RLK_LOGPROB_H
+#define RLK_LOGPROB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct rlk_logprob* rlk_logprob_t;
+typedef void* rlk_stream_t; /* hipStream_t */
+
+typedef enum rlk_status {
+  RLK_OK = 0,
+  RLK_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, inconsistent layout */
+  RLK_ERR_NO_DEVICE = 2,        /* no HIP device, or the device index does not exist */
+  RLK_ERR_UNSUPPORTED_ARCH = 3, /* device is not gfx950 */
+  RLK_ERR_UNSUPPORTED_SHAPE = 4,/* H not a multiple of 64, V not a multiple of the segments ... */
+  RLK_ERR_ALIGNMENT = 5,        /* a device pointer is not 16-byte aligned */
+  RLK_ERR_WORKSPACE = 6,        /* workspace missing or smaller than the size query returned */
+  RLK_ERR_CONTRACT = 7,         /* shard range not on segment boundaries, flags mismatch */
+  RLK_ERR_HIP = 8               /* a HIP runtime call failed (message in rlk_last_error) */
+} rlk_status_t;
+
+/* rlk_logprob_config_t.flags */
+#define RLK_FLAG_RMSNORM 1u /* apply the final RMSNorm (rms_gamma, rms_eps) to hidden first */
+#define RLK_FLAG_ENTROPY 2u /* also produce the per-row entropy of softmax(z') */
+
+/* bits of the device status word */
+#define RLK_DEVICE_STATUS_BAD_TARGET 1u
+
+/* Numeric configuration, fixed at creation. Every field is part of the contract id. */
+typedef struct rlk_logprob_config {
+  int32_t hidden_size;     /* H: a multiple of 64, at most 65536 */
+  int32_t vocab_segments;  /* S_c: 1, 2, 4 or 8 contiguous vocab segments (contract split) */
+  int64_t vocab_size;      /* V: a multiple of S_c; V / S_c at most 2^24 */
+  float inv_temperature;   /* fl32(1/tau) multiplied into every logit; 1.0f = no temperature */
+  float rms_eps;           /* epsilon inside the RMSNorm square root (RLK_FLAG_RMSNORM) */
+  uint32_t flags;          /* RLK_FLAG_* */
+  uint32_t reserved;       /* must be 0 */
+} rlk_logprob_config_t;
+
+/* How the rows and the vocabulary are presented to one forward call. None of it changes a
+ * row's arithmetic; it only changes launches, so outputs are bitwise identical for any layout. */
+typedef struct rlk_layout_desc {
+  int64_t num_rows;             /* T >= 0 */
+  int32_t num_batches;          /* 0 or 1: one packed batch (training layout); >1: ragged batches */
+  int32_t vocab_shards;         /* 1..S_c, dividing S_c: W processed as that many row ranges */
+  const int64_t* batch_offsets; /* host [num_batches+1], ascending, [0] = 0, [nb] = T; or NULL */
+  int64_t row_chunk;            /* >0: each batch runs in launches of at most this many rows */
+  int32_t token_tile;           /* 0 = chosen per launch; or 32, 64, 128, 256 rows per block */
+  int32_t reserved;             /* must be 0 */
+} rlk_layout_desc_t;
+
+/* Per-row, per-vocab-segment partial record, as exchanged between vocab shards.
+ * m = max_v z' over the segment, s = sum_v exp(z' - m), u = sum_v exp(z' - m) (z' - m)
+ * (0 without RLK_FLAG_ENTROPY), tgt = z'[t, y_t] when the segment owns y_t, else NaN. */
+typedef struct rlk_segment_record {
+  float m, s, u, tgt;
+} rlk_segment_record_t;
+
+/* Create a handle bound to HIP device `device`. Checks the device exists and is gfx950 and that
+ * the configuration is supported. Returns RLK_ERR_NO_DEVICE on a machine without a GPU. */
+rlk_status_t rlk_logprob_create(const rlk_logprob_config_t* config, int device,
+                                rlk_logprob_t* out);
+
+/* Destroy a handle (host state only). NULL is accepted. */
+rlk_status_t rlk_logprob_destroy(rlk_logprob_t handle);
+
+/* Host-only, no device needed: bytes of device workspace rlk_logprob_forward needs for this
+ * configuration and layout. */
+rlk_status_t rlk_logprob_workspace_size(const rlk_logprob_config_t* config,
+                                        const rlk_layout_desc_t* layout, size_t* bytes);
+
+/* Host-only, no device needed: validates a layout against a configuration and reports how many
+ * LM-head kernel launches a forward with it makes (row launch groups x vocab shards). */
+rlk_status_t rlk_layout_check(const rlk_logprob_config_t* config,
+                              const rlk_layout_desc_t* layout, int64_t* num_launches);
+
+/* The strict-path forward. hidden: bf16 [T,H]; W_lm: bf16 [V,H]; targets: int32 [T];
+ * rms_gamma: bf16 [H] with RLK_FLAG_RMSNORM, else NULL. Outputs fp32 [T]: logp, lse, and
+ * entropy (required with RLK_FLAG_ENTROPY, else NULL). workspace: device memory of at least
+ * rlk_logprob_workspace_size bytes, 256-byte aligned; its contents on entry do not matter. */
+rlk_status_t rlk_logprob_forward(rlk_logprob_t handle, const void* hidden, const void* W_lm,
+                                 const int32_t* targets, const rlk_layout_desc_t* layout,
+                                 const void* rms_gamma, float* logp, float* lse, float* entropy,
+                                 void* workspace, size_t workspace_bytes, rlk_stream_t stream);
+
+/* Host-only: workspace bytes of rlk_logprob_partials for `num_rows` rows over the vocab range
+ * [vocab_begin, vocab_end). */
+rlk_status_t rlk_logprob_partials_workspace_size(const rlk_logprob_config_t* config,
+                                                 int64_t num_rows, int64_t vocab_begin,
+                                                 int64_t vocab_end, size_t* bytes);
+
+/* One vocab shard's local reduction: W_shard is bf16 [vocab_end - vocab_begin, H], the rows
+ * [vocab_begin, vocab_end) of W_lm; the range must start and end on segment boundaries
+ * (multiples of V / S_c), else RLK_ERR_CONTRACT. Writes records[(s - s0) * num_rows + t] for
+ * every segment s of the range (s0 = vocab_begin / (V / S_c)) and every row t. */
+rlk_status_t rlk_logprob_partials(rlk_logprob_t handle, const void* hidden, const void* W_shard,
+                                  int64_t vocab_begin, int64_t vocab_end,
+                                  const int32_t* targets, int64_t num_rows,
+                                  const void* rms_gamma, rlk_segment_record_t* records,
+                                  void* workspace, size_t workspace_bytes, rlk_stream_t stream);
+
+/* Cross-segment merge in the contract's fixed order: records holds S_c * num_rows records,
+ * segment-major (all segments of the vocabulary, gathered from every shard). Writes logp, lse
+ * and (with RLK_FLAG_ENTROPY) entropy. status: device uint32 that receives the
+ * RLK_DEVICE_STATUS_* bits (OR-ed in), or NULL. */
+rlk_status_t rlk_logprob_merge(rlk_logprob_t handle, const rlk_segment_record_t* records,
+                               const int32_t* targets, int64_t num_rows, float* logp, float* lse,
+                               float* entropy, uint32_t* status, rlk_stream_t stream);
+
+/* Waits for `stream`, then reads the status word a forward left in `workspace`. */
+rlk_status_t rlk_logprob_device_status(rlk_logprob_t handle, const void* workspace,
+                                       rlk_stream_t stream, uint32_t* flags);
+
+/* Contract id of the handle: every constant that decides a result bit. Two handles give
+ * bitwise-identical rows exactly when their contract ids are equal. */
+const char* rlk_logprob_contract_id(rlk_logprob_t handle);
+
+/* Compiler, flags and target the library was built with. */
+const char* rlk_build_fingerprint(void);
+
+const char* rlk_status_string(rlk_status_t status);
+const char* rlk_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RLK_LOGPROB_H */

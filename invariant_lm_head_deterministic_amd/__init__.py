@@ -1,0 +1,211 @@
+"""Strict-path selected-token logprob on MI355X (gfx950): LM head -> log-softmax -> gather.
+
+``Logprob`` marshals torch tensors (device memory, the current stream) into the C ABI of
+``librlk_logprob.so``; all arithmetic runs in the library's HIP kernels. If the library is not
+built, every call raises: there is no CPU or eager fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Sequence
+
+import numpy as np
+
+from . import _lib
+from ._lib import (  # noqa: F401
+    RLK_DEVICE_STATUS_BAD_TARGET,
+    RLK_FLAG_ENTROPY,
+    RLK_FLAG_RMSNORM,
+    RlkError,
+    rlk_build_fingerprint,
+    rlk_layout_check,
+    rlk_logprob_config_t,
+    rlk_logprob_contract_id,
+    rlk_logprob_create,
+    rlk_logprob_destroy,
+    rlk_logprob_device_status,
+    rlk_logprob_forward,
+    rlk_logprob_merge,
+    rlk_logprob_partials,
+    rlk_logprob_partials_workspace_size,
+    rlk_logprob_workspace_size,
+    rlk_layout_desc_t,
+    rlk_segment_record_t,
+    rlk_status_string,
+)
+
+__all__ = ["Logprob", "make_config", "make_layout", "require_library", "RlkError"]
+
+
+def require_library():
+    """Load the HIP library or raise."""
+    return _lib.load()
+
+
+def inv_temperature(tau: float) -> float:
+    """fl32(1/tau): the reciprocal is formed in float64 on the host and rounded once."""
+    return float(np.float32(1.0 / float(tau)))
+
+
+def make_config(hidden_size: int, vocab_size: int, vocab_segments: int = 4,
+                temperature: float = 1.0, rmsnorm: bool = False, rms_eps: float = 1e-6,
+                entropy: bool = False) -> rlk_logprob_config_t:
+    c = rlk_logprob_config_t()
+    c.hidden_size = hidden_size
+    c.vocab_segments = vocab_segments
+    c.vocab_size = vocab_size
+    c.inv_temperature = inv_temperature(temperature)
+    c.rms_eps = rms_eps if rmsnorm else 0.0
+    c.flags = (RLK_FLAG_RMSNORM if rmsnorm else 0) | (RLK_FLAG_ENTROPY if entropy else 0)
+    c.reserved = 0
+    return c
+
+
+def make_layout(num_rows: int, batch_sizes: Sequence[int] | None = None, row_chunk: int = 0,
+                vocab_shards: int = 1, token_tile: int = 0):
+    """A layout descriptor plus the host array its pointer refers to (keep both alive)."""
+    l = rlk_layout_desc_t()
+    l.num_rows = num_rows
+    l.vocab_shards = vocab_shards
+    l.row_chunk = row_chunk
+    l.token_tile = token_tile
+    l.reserved = 0
+    keep = None
+    if batch_sizes is not None and len(batch_sizes) > 1:
+        offs = [0]
+        for s in batch_sizes:
+            offs.append(offs[-1] + int(s))
+        keep = (ctypes.c_int64 * len(offs))(*offs)
+        l.num_batches = len(batch_sizes)
+        l.batch_offsets = ctypes.cast(keep, ctypes.POINTER(ctypes.c_int64))
+    else:
+        l.num_batches = 1
+        l.batch_offsets = None
+    return l, keep
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+class Logprob:
+    """A handle of the C library bound to one device and one numeric configuration."""
+
+    def __init__(self, hidden_size: int, vocab_size: int, vocab_segments: int = 4,
+                 temperature: float = 1.0, rmsnorm: bool = False, rms_eps: float = 1e-6,
+                 entropy: bool = False, device: int = 0):
+        self.config = make_config(hidden_size, vocab_size, vocab_segments, temperature, rmsnorm,
+                                  rms_eps, entropy)
+        self.device = device
+        self.entropy = entropy
+        self.rmsnorm = rmsnorm
+        self.handle = rlk_logprob_create(self.config, device)
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h:
+            try:
+                rlk_logprob_destroy(h)
+            except Exception:
+                pass
+            self.handle = None
+
+    @property
+    def contract_id(self) -> str:
+        return rlk_logprob_contract_id(self.handle)
+
+    def workspace_size(self, num_rows: int, **layout_kw) -> int:
+        layout, _keep = make_layout(num_rows, **layout_kw)
+        return rlk_logprob_workspace_size(self.config, layout)
+
+    def _check(self, t, dtype, name: str):
+        import torch
+
+        if t.device.type != "cuda" or t.device.index != self.device:
+            raise ValueError(f"{name} must be on cuda:{self.device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dtype not in dtype:
+            raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtype}")
+        return torch
+
+    def forward(self, hidden, W, targets, *, batch_sizes=None, row_chunk: int = 0,
+                vocab_shards: int = 1, token_tile: int = 0, gamma=None, workspace=None,
+                out=None, stream=None) -> dict:
+        """Selected-token logprob of every row. hidden [T,H] and W [V,H] bf16 (or int16 bit
+        views), targets int32 [T] (negative = padded). Returns {"logp", "lse"[, "entropy"]}
+        fp32 [T] on the device, enqueued on ``stream`` (default: torch's current stream)."""
+        import torch
+
+        bf = (torch.bfloat16, torch.int16, torch.uint16)
+        self._check(hidden, bf, "hidden")
+        self._check(W, bf, "W")
+        self._check(targets, (torch.int32,), "targets")
+        T = targets.shape[0]
+        if hidden.dim() != 2 or hidden.shape[0] != T or hidden.shape[1] != self.config.hidden_size:
+            raise ValueError("hidden must be [T, H]")
+        if W.dim() != 2 or W.shape[0] != self.config.vocab_size or W.shape[1] != self.config.hidden_size:
+            raise ValueError("W must be [V, H]")
+        if gamma is not None:
+            self._check(gamma, bf, "gamma")
+        layout, keep = make_layout(T, batch_sizes, row_chunk, vocab_shards, token_tile)
+        need = rlk_logprob_workspace_size(self.config, layout)
+        dev = torch.device("cuda", self.device)
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        if out is None:
+            out = {"logp": torch.empty(T, dtype=torch.float32, device=dev),
+                   "lse": torch.empty(T, dtype=torch.float32, device=dev)}
+            if self.entropy:
+                out["entropy"] = torch.empty(T, dtype=torch.float32, device=dev)
+        s = stream if stream is not None else torch.cuda.current_stream(dev)
+        rlk_logprob_forward(self.handle, hidden.data_ptr(), W.data_ptr(), targets.data_ptr(),
+                            layout, _ptr(gamma), out["logp"].data_ptr(), out["lse"].data_ptr(),
+                            _ptr(out.get("entropy")), workspace.data_ptr(),
+                            workspace.numel() * workspace.element_size(), s.cuda_stream)
+        del keep
+        out["_workspace"] = workspace
+        return out
+
+    def device_status(self, workspace, stream=None) -> int:
+        import torch
+
+        s = stream if stream is not None else torch.cuda.current_stream(
+            torch.device("cuda", self.device))
+        return rlk_logprob_device_status(self.handle, workspace.data_ptr(), s.cuda_stream)
+
+    def partials(self, hidden, W_shard, vocab_begin: int, vocab_end: int, targets, *, gamma=None,
+                 records=None, stream=None):
+        """One vocab shard's per-segment records, shape [n_local_segments, T, 4] fp32."""
+        import torch
+
+        T = targets.shape[0]
+        dev = torch.device("cuda", self.device)
+        need = rlk_logprob_partials_workspace_size(self.config, T, vocab_begin, vocab_end)
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        seg_len = self.config.vocab_size // self.config.vocab_segments
+        nloc = (vocab_end - vocab_begin) // seg_len
+        if records is None:
+            records = torch.empty((nloc, T, 4), dtype=torch.float32, device=dev)
+        s = stream if stream is not None else torch.cuda.current_stream(dev)
+        rlk_logprob_partials(self.handle, hidden.data_ptr(), W_shard.data_ptr(), vocab_begin,
+                             vocab_end, targets.data_ptr(), T, _ptr(gamma), records.data_ptr(),
+                             ws.data_ptr(), ws.numel(), s.cuda_stream)
+        return records
+
+    def merge(self, records, targets, *, status=None, stream=None) -> dict:
+        """Merge the records of all segments ([S_c, T, 4] fp32) into logp, lse[, entropy]."""
+        import torch
+
+        T = targets.shape[0]
+        dev = torch.device("cuda", self.device)
+        out = {"logp": torch.empty(T, dtype=torch.float32, device=dev),
+               "lse": torch.empty(T, dtype=torch.float32, device=dev)}
+        if self.entropy:
+            out["entropy"] = torch.empty(T, dtype=torch.float32, device=dev)
+        s = stream if stream is not None else torch.cuda.current_stream(dev)
+        rlk_logprob_merge(self.handle, records.data_ptr(), targets.data_ptr(), T,
+                          out["logp"].data_ptr(), out["lse"].data_ptr(), _ptr(out.get("entropy")),
+                          _ptr(status), s.cuda_stream)
+        return out

@@ -1,0 +1,571 @@
+// Host side of the C ABI: validation, layout planning, workspace carving and launches.
+//
+// Strict mode only: every unsupported case returns an error naming why and enqueues nothing;
+// there is no fallback path (RL-Kernel v0.1.0 summary page, "Numeric execution contract": a
+// strict path either runs the declared contract or reports that it cannot). The layout
+// descriptor only changes which launches are made — the per-row arithmetic is the kernels'
+// (the aihirek.info report, "A vime és az RL-Kernel eltérő feladatot kapott": memory layouts and
+// schedules may differ as long as they do not change the numerics being compared).
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "rlk_internal.h"
+#include "rlk_logprob.h"
+
+#ifndef RLK_BUILD_FLAGS
+#define RLK_BUILD_FLAGS "unknown"
+#endif
+
+#define RLK_API extern "C" __attribute__((visibility("default")))
+
+struct rlk_logprob {
+  rlk_logprob_config_t cfg;
+  int device;
+  std::string contract;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+rlk_status_t fail(rlk_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+rlk_status_t ok() {
+  g_last_error.clear();
+  return RLK_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Geometry {
+  int64_t seg_len;
+  int32_t tiles_per_seg;
+  int32_t n_tiles;
+};
+
+Geometry geometry(const rlk_logprob_config_t& c) {
+  Geometry g;
+  g.seg_len = c.vocab_size / c.vocab_segments;
+  g.tiles_per_seg = (int32_t)((g.seg_len + rlk::kVocabTile - 1) / rlk::kVocabTile);
+  g.n_tiles = g.tiles_per_seg * c.vocab_segments;
+  return g;
+}
+
+rlk_status_t check_config(const rlk_logprob_config_t* c) {
+  if (!c) return fail(RLK_ERR_INVALID_ARGUMENT, "config is NULL");
+  if (c->reserved != 0) return fail(RLK_ERR_INVALID_ARGUMENT, "config.reserved must be 0");
+  if (c->flags & ~(RLK_FLAG_RMSNORM | RLK_FLAG_ENTROPY))
+    return fail(RLK_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", c->flags);
+  if (c->hidden_size <= 0 || c->hidden_size % 64 != 0 || c->hidden_size > 65536)
+    return fail(RLK_ERR_UNSUPPORTED_SHAPE, "hidden_size %d is not a positive multiple of 64 <= 65536",
+                c->hidden_size);
+  const int s = c->vocab_segments;
+  if (s != 1 && s != 2 && s != 4 && s != 8)
+    return fail(RLK_ERR_UNSUPPORTED_SHAPE, "vocab_segments %d is not 1, 2, 4 or 8", s);
+  if (c->vocab_size <= 0 || c->vocab_size % s != 0)
+    return fail(RLK_ERR_UNSUPPORTED_SHAPE, "vocab_size %lld is not a positive multiple of %d",
+                (long long)c->vocab_size, s);
+  if (c->vocab_size / s > (1LL << 24))
+    return fail(RLK_ERR_UNSUPPORTED_SHAPE, "vocab segment longer than 2^24");
+  if (c->vocab_size > 0x7fffffffLL)
+    return fail(RLK_ERR_UNSUPPORTED_SHAPE, "vocab_size does not fit int32 targets");
+  if (!std::isfinite(c->inv_temperature) || !(c->inv_temperature > 0.0f))
+    return fail(RLK_ERR_INVALID_ARGUMENT, "inv_temperature must be finite and > 0");
+  if ((c->flags & RLK_FLAG_RMSNORM) && !(std::isfinite(c->rms_eps) && c->rms_eps >= 0.0f))
+    return fail(RLK_ERR_INVALID_ARGUMENT, "rms_eps must be finite and >= 0");
+  return RLK_OK;
+}
+
+struct RowRange {
+  int64_t begin, end;
+};
+
+// One LM-head launch group: a row range (of one batch chunk) x one vocab shard.
+struct Plan {
+  std::vector<RowRange> batches;          // merge granularity
+  std::vector<std::vector<RowRange>> chunks;  // per batch
+  int32_t shards;
+  int64_t launches;
+};
+
+rlk_status_t plan_layout(const rlk_logprob_config_t& c, const rlk_layout_desc_t* l, Plan* p) {
+  if (!l) return fail(RLK_ERR_INVALID_ARGUMENT, "layout is NULL");
+  if (l->reserved != 0) return fail(RLK_ERR_INVALID_ARGUMENT, "layout.reserved must be 0");
+  if (l->num_rows < 0 || l->num_rows > 0x7fffffffLL)
+    return fail(RLK_ERR_INVALID_ARGUMENT, "num_rows %lld out of range", (long long)l->num_rows);
+  if (l->row_chunk < 0) return fail(RLK_ERR_INVALID_ARGUMENT, "row_chunk < 0");
+  if (l->token_tile != 0 && !rlk::token_tile_supported(l->token_tile))
+    return fail(RLK_ERR_UNSUPPORTED_SHAPE, "token_tile %d is not 0, 32, 64, 128 or 256", l->token_tile);
+  const int32_t ns = l->vocab_shards == 0 ? 1 : l->vocab_shards;
+  if (ns < 1 || ns > c.vocab_segments || c.vocab_segments % ns != 0)
+    return fail(RLK_ERR_CONTRACT, "vocab_shards %d does not divide vocab_segments %d", ns,
+                c.vocab_segments);
+  const int64_t T = l->num_rows;
+  p->batches.clear();
+  p->chunks.clear();
+  if (l->num_batches <= 1) {
+    if (l->num_batches == 1 && l->batch_offsets &&
+        (l->batch_offsets[0] != 0 || l->batch_offsets[1] != T))
+      return fail(RLK_ERR_INVALID_ARGUMENT, "single batch offsets must be [0, num_rows]");
+    if (l->num_batches < 0) return fail(RLK_ERR_INVALID_ARGUMENT, "num_batches < 0");
+    p->batches.push_back({0, T});
+  } else {
+    const int64_t* o = l->batch_offsets;
+    if (!o) return fail(RLK_ERR_INVALID_ARGUMENT, "num_batches > 1 needs batch_offsets");
+    if (o[0] != 0 || o[l->num_batches] != T)
+      return fail(RLK_ERR_INVALID_ARGUMENT, "batch_offsets must start at 0 and end at num_rows");
+    for (int32_t b = 0; b < l->num_batches; ++b) {
+      if (o[b + 1] < o[b]) return fail(RLK_ERR_INVALID_ARGUMENT, "batch_offsets not ascending");
+      p->batches.push_back({o[b], o[b + 1]});
+    }
+  }
+  p->shards = ns;
+  p->launches = 0;
+  for (const RowRange& b : p->batches) {
+    std::vector<RowRange> ch;
+    const int64_t n = b.end - b.begin;
+    const int64_t step = l->row_chunk > 0 ? l->row_chunk : std::max<int64_t>(n, 1);
+    for (int64_t r = b.begin; r < b.end; r += step) ch.push_back({r, std::min(b.end, r + step)});
+    p->launches += (int64_t)ch.size() * ns;
+    p->chunks.push_back(std::move(ch));
+  }
+  return RLK_OK;
+}
+
+// Workspace map (offsets in bytes, each 256-aligned).
+struct WsMap {
+  size_t status, tgt, pm, ps, pu, rec, y, total;
+};
+
+WsMap ws_map(const rlk_logprob_config_t& c, int64_t rows, int32_t n_tiles, int32_t n_rec_seg) {
+  const bool ent = c.flags & RLK_FLAG_ENTROPY;
+  const bool rms = c.flags & RLK_FLAG_RMSNORM;
+  WsMap m;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = round_up(off + bytes, 256);
+    return at;
+  };
+  const size_t rowsz = (size_t)std::max<int64_t>(rows, 1);
+  m.status = take(4);
+  m.tgt = take(rowsz * 4);
+  m.pm = take((size_t)n_tiles * rowsz * 4);
+  m.ps = take((size_t)n_tiles * rowsz * 4);
+  m.pu = ent ? take((size_t)n_tiles * rowsz * 4) : 0;
+  m.rec = n_rec_seg ? take((size_t)n_rec_seg * rowsz * sizeof(rlk_segment_record_t)) : 0;
+  m.y = rms ? take(rowsz * (size_t)c.hidden_size * 2) : 0;
+  m.total = off;
+  return m;
+}
+
+int auto_token_tile(int64_t rows) {
+  if (rows >= 512) return 256;
+  if (rows > 64) return 128;
+  if (rows > 32) return 64;
+  return 32;
+}
+
+struct DeviceGuard {
+  int prev = -1;
+  bool changed = false;
+  hipError_t err = hipSuccess;
+  explicit DeviceGuard(int dev) {
+    err = hipGetDevice(&prev);
+    if (err == hipSuccess && prev != dev) {
+      err = hipSetDevice(dev);
+      changed = err == hipSuccess;
+    }
+  }
+  ~DeviceGuard() {
+    if (changed) (void)hipSetDevice(prev);
+  }
+};
+
+rlk_status_t hip_fail(hipError_t e, const char* what) {
+  return fail(RLK_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// RMSNorm (optional) then the LM-head tile kernel over rows [r0, r1) and segments [s0, s1).
+rlk_status_t run_rows(const rlk_logprob* h, const Geometry& g, const void* hidden, const void* W,
+                      int64_t w_row0, const int32_t* targets, const void* gamma, const WsMap& m,
+                      uint8_t* ws, int64_t ld, int32_t g_base, int64_t r0, int64_t r1, int s0,
+                      int s1, int token_tile, bool do_norm, hipStream_t st) {
+  const rlk_logprob_config_t& c = h->cfg;
+  const int64_t n = r1 - r0;
+  if (n <= 0) return RLK_OK;
+  const uint16_t* hid = static_cast<const uint16_t*>(hidden);
+  if (c.flags & RLK_FLAG_RMSNORM) {
+    uint16_t* y = reinterpret_cast<uint16_t*>(ws + m.y);
+    if (do_norm) {
+      rlk::RmsArgs ra;
+      ra.x = hid + r0 * (int64_t)c.hidden_size;
+      ra.gamma = static_cast<const uint16_t*>(gamma);
+      ra.y = y + r0 * (int64_t)c.hidden_size;
+      ra.rows = (int32_t)n;
+      ra.H = c.hidden_size;
+      ra.inv_H = 1.0f / (float)c.hidden_size;
+      ra.eps = c.rms_eps;
+      hipError_t e = rlk::launch_rmsnorm(ra, st);
+      if (e != hipSuccess) return hip_fail(e, "rmsnorm launch");
+    }
+    hid = y;
+  }
+  const bool ent = c.flags & RLK_FLAG_ENTROPY;
+  rlk::LmheadArgs a;
+  a.hidden = hid + r0 * (int64_t)c.hidden_size;
+  a.W = static_cast<const uint16_t*>(W);
+  a.targets = targets + r0;
+  a.part_m = reinterpret_cast<float*>(ws + m.pm) + r0;
+  a.part_s = reinterpret_cast<float*>(ws + m.ps) + r0;
+  a.part_u = ent ? reinterpret_cast<float*>(ws + m.pu) + r0 : nullptr;
+  a.tgt = reinterpret_cast<float*>(ws + m.tgt) + r0;
+  a.ld = ld;
+  a.w_row0 = w_row0;
+  a.seg_len = g.seg_len;
+  a.rows = (int32_t)n;
+  a.H = c.hidden_size;
+  a.tiles_per_seg = g.tiles_per_seg;
+  a.seg_begin = s0;
+  a.n_seg = s1 - s0;
+  a.g_base = g_base;
+  a.inv_tau = c.inv_temperature;
+  const int bt = token_tile ? token_tile : auto_token_tile(n);
+  hipError_t e = rlk::launch_lmhead(a, bt, ent, st);
+  if (e != hipSuccess) return hip_fail(e, "lm-head launch");
+  return RLK_OK;
+}
+
+}  // namespace
+
+// ============================================================================================
+RLK_API const char* rlk_status_string(rlk_status_t s) {
+  switch (s) {
+    case RLK_OK: return "ok";
+    case RLK_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case RLK_ERR_NO_DEVICE: return "no HIP device";
+    case RLK_ERR_UNSUPPORTED_ARCH: return "unsupported GPU architecture (gfx950 only)";
+    case RLK_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
+    case RLK_ERR_ALIGNMENT: return "misaligned pointer";
+    case RLK_ERR_WORKSPACE: return "workspace missing or too small";
+    case RLK_ERR_CONTRACT: return "numeric contract violated";
+    case RLK_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+RLK_API const char* rlk_last_error(void) { return g_last_error.c_str(); }
+
+RLK_API const char* rlk_build_fingerprint(void) {
+  static const std::string fp = std::string("rlk_logprob contract v") +
+                                std::to_string(rlk::kContractVersion) +
+                                "; target gfx950; compiler " + __clang_version__ +
+                                "; flags " + RLK_BUILD_FLAGS;
+  return fp.c_str();
+}
+
+RLK_API rlk_status_t rlk_logprob_create(const rlk_logprob_config_t* config, int device,
+                                        rlk_logprob_t* out) {
+  if (!out) return fail(RLK_ERR_INVALID_ARGUMENT, "out is NULL");
+  *out = nullptr;
+  rlk_status_t st = check_config(config);
+  if (st != RLK_OK) return st;
+  int count = 0;
+  hipError_t e = hipGetDeviceCount(&count);
+  if (e != hipSuccess || count <= 0) return fail(RLK_ERR_NO_DEVICE, "no HIP device visible");
+  if (device < 0 || device >= count)
+    return fail(RLK_ERR_NO_DEVICE, "device %d does not exist (%d visible)", device, count);
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, device);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(RLK_ERR_UNSUPPORTED_ARCH, "device %d is %s, not gfx950", device, prop.gcnArchName);
+  rlk_logprob* h = new (std::nothrow) rlk_logprob;
+  if (!h) return fail(RLK_ERR_INVALID_ARGUMENT, "out of host memory");
+  h->cfg = *config;
+  h->device = device;
+  uint32_t itb;
+  std::memcpy(&itb, &config->inv_temperature, 4);
+  uint32_t epsb;
+  std::memcpy(&epsb, &config->rms_eps, 4);
+  char buf[512];
+  snprintf(buf, sizeof(buf),
+           "rlk-logprob/v%d;mfma=v_mfma_f32_32x32x16_bf16;kstep=16;bv=%d;H=%d;V=%lld;Sc=%d;"
+           "intile=seq16+pair8+half;segfold=seq;segmerge=pair;exp=v_exp_f32(x*0x3fb8aa3b);"
+           "log=v_log_f32*0x3f317218;inv_tau=0x%08x;rms=%d;rms_eps=0x%08x;rsq=v_rsq_f32;"
+           "rms_tree=lane-seq8+xor32..1;entropy=%d;contract=off",
+           rlk::kContractVersion, rlk::kVocabTile, config->hidden_size,
+           (long long)config->vocab_size, config->vocab_segments, itb,
+           (config->flags & RLK_FLAG_RMSNORM) ? 1 : 0,
+           (config->flags & RLK_FLAG_RMSNORM) ? epsb : 0u,
+           (config->flags & RLK_FLAG_ENTROPY) ? 1 : 0);
+  h->contract = buf;
+  *out = h;
+  return ok();
+}
+
+RLK_API rlk_status_t rlk_logprob_destroy(rlk_logprob_t h) {
+  delete h;
+  return ok();
+}
+
+RLK_API const char* rlk_logprob_contract_id(rlk_logprob_t h) { return h ? h->contract.c_str() : ""; }
+
+RLK_API rlk_status_t rlk_layout_check(const rlk_logprob_config_t* config,
+                                      const rlk_layout_desc_t* layout, int64_t* num_launches) {
+  rlk_status_t st = check_config(config);
+  if (st != RLK_OK) return st;
+  Plan p;
+  st = plan_layout(*config, layout, &p);
+  if (st != RLK_OK) return st;
+  if (num_launches) *num_launches = p.launches;
+  return ok();
+}
+
+RLK_API rlk_status_t rlk_logprob_workspace_size(const rlk_logprob_config_t* config,
+                                                const rlk_layout_desc_t* layout, size_t* bytes) {
+  if (!bytes) return fail(RLK_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  rlk_status_t st = check_config(config);
+  if (st != RLK_OK) return st;
+  Plan p;
+  st = plan_layout(*config, layout, &p);
+  if (st != RLK_OK) return st;
+  const Geometry g = geometry(*config);
+  *bytes = ws_map(*config, layout->num_rows, g.n_tiles, config->vocab_segments).total;
+  return ok();
+}
+
+RLK_API rlk_status_t rlk_logprob_forward(rlk_logprob_t h, const void* hidden, const void* W_lm,
+                                         const int32_t* targets, const rlk_layout_desc_t* layout,
+                                         const void* rms_gamma, float* logp, float* lse,
+                                         float* entropy, void* workspace, size_t workspace_bytes,
+                                         rlk_stream_t stream) {
+  if (!h) return fail(RLK_ERR_INVALID_ARGUMENT, "handle is NULL");
+  const rlk_logprob_config_t& c = h->cfg;
+  Plan p;
+  rlk_status_t st = plan_layout(c, layout, &p);
+  if (st != RLK_OK) return st;
+  const int64_t T = layout->num_rows;
+  const bool ent = c.flags & RLK_FLAG_ENTROPY;
+  const bool rms = c.flags & RLK_FLAG_RMSNORM;
+  if (T > 0) {
+    if (!hidden || !W_lm || !targets || !logp || !lse)
+      return fail(RLK_ERR_INVALID_ARGUMENT, "hidden, W_lm, targets, logp and lse are required");
+    if (ent && !entropy) return fail(RLK_ERR_INVALID_ARGUMENT, "entropy output required");
+    if (rms && !rms_gamma) return fail(RLK_ERR_INVALID_ARGUMENT, "rms_gamma required");
+    if (!aligned16(hidden) || !aligned16(W_lm) || !aligned16(targets) || !aligned16(logp) ||
+        !aligned16(lse) || (entropy && !aligned16(entropy)) || (rms_gamma && !aligned16(rms_gamma)))
+      return fail(RLK_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
+  }
+  if (!ent && entropy) return fail(RLK_ERR_CONTRACT, "entropy given but RLK_FLAG_ENTROPY not set");
+  if (!rms && rms_gamma) return fail(RLK_ERR_CONTRACT, "rms_gamma given but RLK_FLAG_RMSNORM not set");
+  const Geometry g = geometry(c);
+  const WsMap m = ws_map(c, T, g.n_tiles, c.vocab_segments);
+  if (!workspace || workspace_bytes < m.total)
+    return fail(RLK_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", m.total, workspace_bytes);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(RLK_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
+  DeviceGuard guard(h->device);
+  if (guard.err != hipSuccess) return hip_fail(guard.err, "hipSetDevice");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint32_t* status = reinterpret_cast<uint32_t*>(ws + m.status);
+  hipError_t e = rlk::launch_clear_status(status, s);
+  if (e != hipSuccess) return hip_fail(e, "status clear launch");
+  if (T == 0) return ok();
+
+  const int seg_per_shard = c.vocab_segments / p.shards;
+  const int64_t H = c.hidden_size;
+  for (size_t b = 0; b < p.batches.size(); ++b) {
+    for (const RowRange& ch : p.chunks[b]) {
+      for (int sh = 0; sh < p.shards; ++sh) {
+        const int s0 = sh * seg_per_shard, s1 = s0 + seg_per_shard;
+        const int64_t w_row0 = (int64_t)s0 * g.seg_len;
+        const void* Wsh = static_cast<const uint16_t*>(W_lm) + w_row0 * H;
+        st = run_rows(h, g, hidden, Wsh, w_row0, targets, rms_gamma, m, ws, T, 0, ch.begin,
+                      ch.end, s0, s1, layout->token_tile, sh == 0, s);
+        if (st != RLK_OK) return st;
+      }
+    }
+    const RowRange& br = p.batches[b];
+    const int64_t n = br.end - br.begin;
+    if (n == 0) continue;
+    rlk::FoldArgs f;
+    f.part_m = reinterpret_cast<const float*>(ws + m.pm) + br.begin;
+    f.part_s = reinterpret_cast<const float*>(ws + m.ps) + br.begin;
+    f.part_u = ent ? reinterpret_cast<const float*>(ws + m.pu) + br.begin : nullptr;
+    f.tgt = reinterpret_cast<const float*>(ws + m.tgt) + br.begin;
+    f.targets = targets + br.begin;
+    f.rec = reinterpret_cast<rlk_segment_record_t*>(ws + m.rec) + br.begin;
+    f.ld = T;
+    f.rec_ld = T;
+    f.seg_len = g.seg_len;
+    f.rows = (int32_t)n;
+    f.tiles_per_seg = g.tiles_per_seg;
+    f.seg_begin = 0;
+    f.n_seg = c.vocab_segments;
+    f.g_base = 0;
+    e = rlk::launch_fold(f, ent, s);
+    if (e != hipSuccess) return hip_fail(e, "segment fold launch");
+    rlk::MergeArgs mg;
+    mg.rec = reinterpret_cast<const rlk_segment_record_t*>(ws + m.rec) + br.begin;
+    mg.targets = targets + br.begin;
+    mg.logp = logp + br.begin;
+    mg.lse = lse + br.begin;
+    mg.entropy = ent ? entropy + br.begin : nullptr;
+    mg.status = status;
+    mg.rec_ld = T;
+    mg.seg_len = g.seg_len;
+    mg.vocab = c.vocab_size;
+    mg.rows = (int32_t)n;
+    mg.n_seg = c.vocab_segments;
+    e = rlk::launch_merge(mg, ent, s);
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+  }
+  return ok();
+}
+
+RLK_API rlk_status_t rlk_logprob_partials_workspace_size(const rlk_logprob_config_t* config,
+                                                         int64_t num_rows, int64_t vocab_begin,
+                                                         int64_t vocab_end, size_t* bytes) {
+  if (!bytes) return fail(RLK_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  rlk_status_t st = check_config(config);
+  if (st != RLK_OK) return st;
+  if (num_rows < 0 || num_rows > 0x7fffffffLL)
+    return fail(RLK_ERR_INVALID_ARGUMENT, "num_rows out of range");
+  const Geometry g = geometry(*config);
+  if (vocab_begin < 0 || vocab_end > config->vocab_size || vocab_end <= vocab_begin ||
+      vocab_begin % g.seg_len != 0 || vocab_end % g.seg_len != 0)
+    return fail(RLK_ERR_CONTRACT, "vocab range [%lld, %lld) is not on segment boundaries of %lld",
+                (long long)vocab_begin, (long long)vocab_end, (long long)g.seg_len);
+  const int nseg = (int)((vocab_end - vocab_begin) / g.seg_len);
+  *bytes = ws_map(*config, num_rows, nseg * g.tiles_per_seg, 0).total;
+  return ok();
+}
+
+RLK_API rlk_status_t rlk_logprob_partials(rlk_logprob_t h, const void* hidden,
+                                          const void* W_shard, int64_t vocab_begin,
+                                          int64_t vocab_end, const int32_t* targets,
+                                          int64_t num_rows, const void* rms_gamma,
+                                          rlk_segment_record_t* records, void* workspace,
+                                          size_t workspace_bytes, rlk_stream_t stream) {
+  if (!h) return fail(RLK_ERR_INVALID_ARGUMENT, "handle is NULL");
+  const rlk_logprob_config_t& c = h->cfg;
+  size_t need = 0;
+  rlk_status_t st = rlk_logprob_partials_workspace_size(&c, num_rows, vocab_begin, vocab_end, &need);
+  if (st != RLK_OK) return st;
+  const bool ent = c.flags & RLK_FLAG_ENTROPY;
+  const bool rms = c.flags & RLK_FLAG_RMSNORM;
+  if (num_rows > 0) {
+    if (!hidden || !W_shard || !targets || !records)
+      return fail(RLK_ERR_INVALID_ARGUMENT, "hidden, W_shard, targets and records are required");
+    if (rms && !rms_gamma) return fail(RLK_ERR_INVALID_ARGUMENT, "rms_gamma required");
+    if (!aligned16(hidden) || !aligned16(W_shard) || !aligned16(targets) || !aligned16(records) ||
+        (rms_gamma && !aligned16(rms_gamma)))
+      return fail(RLK_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
+  }
+  if (!rms && rms_gamma) return fail(RLK_ERR_CONTRACT, "rms_gamma given but RLK_FLAG_RMSNORM not set");
+  if (!workspace || workspace_bytes < need)
+    return fail(RLK_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(RLK_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
+  if (num_rows == 0) return ok();
+  DeviceGuard guard(h->device);
+  if (guard.err != hipSuccess) return hip_fail(guard.err, "hipSetDevice");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Geometry g = geometry(c);
+  const int s0 = (int)(vocab_begin / g.seg_len), s1 = (int)(vocab_end / g.seg_len);
+  const WsMap m = ws_map(c, num_rows, (s1 - s0) * g.tiles_per_seg, 0);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const int g_base = s0 * g.tiles_per_seg;
+  st = run_rows(h, g, hidden, W_shard, vocab_begin, targets, rms_gamma, m, ws, num_rows, g_base, 0,
+                num_rows, s0, s1, 0, true, s);
+  if (st != RLK_OK) return st;
+  rlk::FoldArgs f;
+  f.part_m = reinterpret_cast<const float*>(ws + m.pm);
+  f.part_s = reinterpret_cast<const float*>(ws + m.ps);
+  f.part_u = ent ? reinterpret_cast<const float*>(ws + m.pu) : nullptr;
+  f.tgt = reinterpret_cast<const float*>(ws + m.tgt);
+  f.targets = targets;
+  f.rec = records;
+  f.ld = num_rows;
+  f.rec_ld = num_rows;
+  f.seg_len = g.seg_len;
+  f.rows = (int32_t)num_rows;
+  f.tiles_per_seg = g.tiles_per_seg;
+  f.seg_begin = s0;
+  f.n_seg = s1 - s0;
+  f.g_base = g_base;
+  hipError_t e = rlk::launch_fold(f, ent, s);
+  if (e != hipSuccess) return hip_fail(e, "segment fold launch");
+  return ok();
+}
+
+RLK_API rlk_status_t rlk_logprob_merge(rlk_logprob_t h, const rlk_segment_record_t* records,
+                                       const int32_t* targets, int64_t num_rows, float* logp,
+                                       float* lse, float* entropy, uint32_t* status,
+                                       rlk_stream_t stream) {
+  if (!h) return fail(RLK_ERR_INVALID_ARGUMENT, "handle is NULL");
+  const rlk_logprob_config_t& c = h->cfg;
+  const bool ent = c.flags & RLK_FLAG_ENTROPY;
+  if (num_rows < 0 || num_rows > 0x7fffffffLL)
+    return fail(RLK_ERR_INVALID_ARGUMENT, "num_rows out of range");
+  if (num_rows == 0) return ok();
+  if (!records || !targets || !logp || !lse)
+    return fail(RLK_ERR_INVALID_ARGUMENT, "records, targets, logp and lse are required");
+  if (ent && !entropy) return fail(RLK_ERR_INVALID_ARGUMENT, "entropy output required");
+  if (!ent && entropy) return fail(RLK_ERR_CONTRACT, "entropy given but RLK_FLAG_ENTROPY not set");
+  if (!aligned16(records) || !aligned16(targets) || !aligned16(logp) || !aligned16(lse) ||
+      (entropy && !aligned16(entropy)) || (reinterpret_cast<uintptr_t>(status) & 3u))
+    return fail(RLK_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
+  DeviceGuard guard(h->device);
+  if (guard.err != hipSuccess) return hip_fail(guard.err, "hipSetDevice");
+  const Geometry g = geometry(c);
+  rlk::MergeArgs mg;
+  mg.rec = records;
+  mg.targets = targets;
+  mg.logp = logp;
+  mg.lse = lse;
+  mg.entropy = entropy;
+  mg.status = status;
+  mg.rec_ld = num_rows;
+  mg.seg_len = g.seg_len;
+  mg.vocab = c.vocab_size;
+  mg.rows = (int32_t)num_rows;
+  mg.n_seg = c.vocab_segments;
+  hipError_t e = rlk::launch_merge(mg, ent, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  return ok();
+}
+
+RLK_API rlk_status_t rlk_logprob_device_status(rlk_logprob_t h, const void* workspace,
+                                               rlk_stream_t stream, uint32_t* flags) {
+  if (!h || !workspace || !flags) return fail(RLK_ERR_INVALID_ARGUMENT, "NULL argument");
+  DeviceGuard guard(h->device);
+  if (guard.err != hipSuccess) return hip_fail(guard.err, "hipSetDevice");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  uint32_t v = 0;
+  e = hipMemcpy(&v, workspace, 4, hipMemcpyDeviceToHost);  // status word sits at offset 0
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy status");
+  *flags = v;
+  return ok();
+}

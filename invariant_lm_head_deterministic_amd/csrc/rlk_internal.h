@@ -1,0 +1,88 @@
+// Internal interface between the host planner (rlk_host.hip) and the kernels (rlk_kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rlk_logprob.h"
+
+namespace rlk {
+
+// ---- numeric contract v1 (every constant here decides result bits) ----
+constexpr int kVocabTile = 256;   // BV: vocab tile width, tiles start at each segment's start
+constexpr int kKStage = 64;       // K elements staged per LDS buffer (4 MFMA steps of 16)
+constexpr int kMaxSegments = 8;   // S_c in {1, 2, 4, 8}
+constexpr int kContractVersion = 1;
+
+// Arguments of the LM-head tile kernel (one launch = a row range x a range of whole segments).
+struct LmheadArgs {
+  const uint16_t* hidden;   // bf16 [rows, H], launch row 0
+  const uint16_t* W;        // bf16 rows of W_lm starting at global vocab index w_row0
+  const int32_t* targets;   // [rows], launch row 0
+  float* part_m;            // [tiles][ld] tile maxima, row index already at launch row 0
+  float* part_s;            // [tiles][ld] tile sums of exp(z' - m)
+  float* part_u;            // [tiles][ld] tile sums of exp(z' - m) (z' - m), or null
+  float* tgt;               // [ld] owner-written target logit z'[t, y_t]
+  int64_t ld;               // row stride of the partial arrays
+  int64_t w_row0;           // global vocab index of W's row 0
+  int64_t seg_len;          // V / S_c
+  int32_t rows;             // rows in this launch
+  int32_t H;
+  int32_t tiles_per_seg;    // ceil(seg_len / kVocabTile)
+  int32_t seg_begin;        // first segment of this launch
+  int32_t n_seg;            // segments in this launch
+  int32_t g_base;           // global tile index stored at partial-array row 0
+  float inv_tau;
+};
+
+struct FoldArgs {
+  const float* part_m;
+  const float* part_s;
+  const float* part_u;      // null without entropy
+  const float* tgt;
+  const int32_t* targets;
+  rlk_segment_record_t* rec;  // [n_seg][rec_ld]
+  int64_t ld;
+  int64_t rec_ld;
+  int64_t seg_len;
+  int32_t rows;
+  int32_t tiles_per_seg;
+  int32_t seg_begin;
+  int32_t n_seg;
+  int32_t g_base;
+};
+
+struct MergeArgs {
+  const rlk_segment_record_t* rec;  // [n_seg][rec_ld], all segments of the vocabulary
+  const int32_t* targets;
+  float* logp;
+  float* lse;
+  float* entropy;           // null without entropy
+  uint32_t* status;         // null allowed
+  int64_t rec_ld;
+  int64_t seg_len;
+  int64_t vocab;
+  int32_t rows;
+  int32_t n_seg;
+};
+
+struct RmsArgs {
+  const uint16_t* x;        // bf16 [rows, H]
+  const uint16_t* gamma;    // bf16 [H]
+  uint16_t* y;              // bf16 [rows, H]
+  int32_t rows;
+  int32_t H;
+  float inv_H;              // fl32(1/H)
+  float eps;
+};
+
+// Token-tile widths the LM-head kernel is built for.
+bool token_tile_supported(int bt);
+
+hipError_t launch_lmhead(const LmheadArgs& a, int token_tile, bool entropy, hipStream_t s);
+hipError_t launch_fold(const FoldArgs& a, bool entropy, hipStream_t s);
+hipError_t launch_merge(const MergeArgs& a, bool entropy, hipStream_t s);
+hipError_t launch_rmsnorm(const RmsArgs& a, hipStream_t s);
+hipError_t launch_clear_status(uint32_t* status, hipStream_t s);
+
+}  // namespace rlk

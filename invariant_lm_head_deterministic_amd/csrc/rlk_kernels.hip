@@ -1,0 +1,565 @@
+// HIP kernels of the strict-path selected-token logprob, for gfx950 (MI355X) only.
+//
+// Numeric contract v1. Every result bit of a row is decided by the rules below and by nothing
+// else: not by the row's position in a launch, the launch's row count, the token-tile width,
+// the grid, the number of vocab shards, or which CU or XCD ran a block. The pages ask for a
+// forward whose inputs, split, merge order, precisions, rounding points and primitives are all
+// fixed (RL-Kernel v0.1.0 summary page, "Numeric execution contract"; kongchang.com article,
+// "four key links"); these are our choices for each.
+//
+//  C1 logit. z[t,v] is one fp32 accumulator chain of v_mfma_f32_32x32x16_bf16 steps starting at
+//     +0: step i (i = 0 .. H/16-1, ascending) feeds K indices 16i .. 16i+15, lanes 0-31 of the
+//     instruction carrying 16i+0..7 and lanes 32-63 carrying 16i+8..15 for both operands.
+//     No split-K, no atomics (the ROCm fixes list on the RL-Kernel page: a deterministic
+//     MFMA-based GEMM; K-dim reduction and accumulation precision in the boundary table).
+//  C2 temperature. z' = z * inv_temperature in fp32 (skipped when it is 1.0f: x * 1.0f == x).
+//  C3 vocab split. The vocabulary is S_c contiguous segments of V/S_c; each segment is cut into
+//     tiles of 256 columns from its own start, the last one partial (the "actual vocab range"
+//     and "local reduction" of the "Linear logprob" boundary row).
+//  C4 tile max. m = max of z' over the tile's columns (exact; order-free).
+//  C5 tile sum. e(v) = EXP(z'(v) - m). The tile's 256 columns form 8 blocks of 32 (b = 0..7)
+//     and two halves h in {0,1}; block b, half h holds the 16 columns
+//     32b + 8(r>>2) + 4h + (r&3), r = 0..15 (the MFMA result-register order). Then
+//        p[b][h] = (((e_r0 + e_r1) + e_r2) + ... ) + e_r15          (sequential in r)
+//        P[h]    = ((p0 + p1) + (p2 + p3)) + ((p4 + p5) + (p6 + p7))  (pairwise in b)
+//        s       = P[0] + P[1]
+//     Columns past the end of a partial tile contribute exactly +0. (nxbn.cn blog, §3.2 and
+//     §4.3: sequential sums inside a thread, then a fixed tree; fp32 intermediates.)
+//  C6 entropy term (optional). u uses the same tree with terms e(v) * (z'(v) - m).
+//  C7 target ownership. The one tile whose columns contain y_t writes z'[t, y_t] as computed
+//     in C1-C2 ("target ownership" in the "Linear logprob" boundary row); nothing is summed.
+//  C8 segment fold. M_s = max_j m_j; S_s = sequential sum over tiles j ascending of
+//     s_j * EXP(m_j - M_s); U_s = sequential sum of (u_j + s_j * (m_j - M_s)) * EXP(m_j - M_s).
+//  C9 cross-segment merge. M = max_s M_s; S and U are balanced pairwise trees in segment order
+//     of S_s * EXP(M_s - M) and (U_s + S_s * (M_s - M)) * EXP(M_s - M) (S_c = 4:
+//     (a0 + a1) + (a2 + a3)) — the "cross-rank LSE merge" in a fixed order.
+//  C10 outputs. lse = M + LOG(S); logp = z'_y - lse; entropy = LOG(S) - U / S; padded rows
+//     (y < 0) write +0; y >= V writes NaN and sets a status bit.
+//  C11 primitives (one exp, one log, one rsqrt; the "primitives" item of the contract):
+//     EXP(x) = v_exp_f32(x * 0x1.715476p+0f), LOG(x) = v_log_f32(x) * 0x1.62e430p-1f,
+//     RSQ(x) = v_rsq_f32(x). Every other operation is one IEEE fp32 operation, rounded to
+//     nearest even; the library is built with -ffp-contract=off so nothing is fused (nxbn.cn
+//     blog, §3.4 and §4.3).
+//  C12 RMSNorm (optional). ss = sum of x_k^2 in fp32 — lane l of a 64-wide wave takes the
+//     8-element groups l, l+64, l+128, ... in order, sequentially — then a butterfly over lanes
+//     with xor distances 32, 16, 8, 4, 2, 1; r = RSQ(ss * fl32(1/H) + eps);
+//     y_k = bf16_rne((x_k * r) * gamma_k) (the "RMSNorm" boundary row: reduction domain,
+//     epsilon, output boundary; wave64 shuffle steps in a fixed order, nxbn.cn blog §3.2).
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "rlk_internal.h"
+
+namespace rlk {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 0x1.715476p+0f;  // fl32(log2(e))
+constexpr float kLn2 = 0x1.62e430p-1f;    // fl32(ln(2))
+constexpr int kRowBytes = kKStage * 2;    // bytes of one staged row (128)
+
+__device__ __forceinline__ float c_exp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+__device__ __forceinline__ float c_log(float x) { return __builtin_amdgcn_logf(x) * kLn2; }
+__device__ __forceinline__ float c_rsq(float x) { return __builtin_amdgcn_rsqf(x); }
+
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// Byte offset of 16-byte piece c (0..7) of staged row `row`: pieces are XOR-swizzled by the
+// row's low 3 bits so that the 8 rows read together by a fragment load hit distinct banks.
+__device__ __forceinline__ int lds_off(int row, int c) { return row * kRowBytes + ((c ^ (row & 7)) << 4); }
+
+// Balanced pairwise sum of N = 2^k values in index order (the C5/C9 tree).
+template <int N>
+__device__ __forceinline__ float tree_sum(const float* v) {
+  if constexpr (N == 1) {
+    return v[0];
+  } else {
+    float w[N / 2];
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) w[i] = v[2 * i] + v[2 * i + 1];
+    return tree_sum<N / 2>(w);
+  }
+}
+
+// --------------------------------------------------------------------------------------------
+// K1: LM-head tile kernel. One block = one vocab tile (256 columns of one segment) x BT rows.
+// Waves: VW split the tile's 8 column blocks, TW split the rows; each wave owns VB = 8/VW column
+// blocks x NTB row blocks of 32, as 32x32 MFMA result tiles (vocab = MFMA rows, tokens = MFMA
+// columns, so each lane holds one token and 16 vocab columns per block: the per-token vocab
+// reduction is lane-local apart from one half-swap and, for VW > 1, one LDS exchange).
+// --------------------------------------------------------------------------------------------
+template <int VW, int TW, int NTB, bool ENT, bool TEMP>
+__global__ void __launch_bounds__(64 * VW * TW)
+k_lmhead(const LmheadArgs a) {
+  constexpr int NWAVES = VW * TW;
+  constexpr int NT = 64 * NWAVES;
+  constexpr int BT = 32 * NTB * TW;
+  constexpr int VB = 8 / VW;
+  constexpr int WP = kVocabTile * 8 / NT;  // 16-byte pieces of a W stage per thread
+  constexpr int HP = BT * 8 / NT;          // 16-byte pieces of a hidden stage per thread
+  static_assert(VB * VW == 8 && WP * NT == kVocabTile * 8 && HP * NT == BT * 8, "tiling");
+
+  __shared__ __attribute__((aligned(16))) uint8_t lds_w[2][kVocabTile * kRowBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_h[2][BT * kRowBytes];
+  __shared__ float red_m[VW > 1 ? VW : 1][BT];
+  __shared__ float red_s[VW > 1 ? VW : 1][2][BT];
+  __shared__ float red_u[(VW > 1 && ENT) ? VW : 1][2][BT];
+
+  // ---- block -> (vocab tile, row tile), XCD-aware: consecutive block ids go round-robin to
+  // the 8 XCDs, so remap them so that each XCD walks a contiguous range of vocab tiles, a group
+  // of 4 vocab tiles at a time across all row tiles (W tiles and hidden tiles shared in L2).
+  const int n_vt = a.n_seg * a.tiles_per_seg;
+  const int n_tt = (a.rows + BT - 1) / BT;
+  const int64_t n_items = (int64_t)n_vt * n_tt;
+  const int64_t per_xcd = (int64_t)gridDim.x / 8;
+  const int64_t L = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (L >= n_items) return;
+  constexpr int GV = 4;
+  const int64_t grp = L / ((int64_t)GV * n_tt);
+  const int first_v = (int)(grp * GV);
+  const int gsz = min(GV, n_vt - first_v);
+  const int64_t within = L - grp * GV * n_tt;
+  const int vt = first_v + (int)(within % gsz);
+  const int tt = (int)(within / gsz);
+
+  const int seg = a.seg_begin + vt / a.tiles_per_seg;
+  const int jt = vt % a.tiles_per_seg;
+  const int64_t tile_start = (int64_t)seg * a.seg_len + (int64_t)jt * kVocabTile;
+  const int tile_len = (int)min((int64_t)kVocabTile, a.seg_len - (int64_t)jt * kVocabTile);
+  const int gtile = seg * a.tiles_per_seg + jt;
+  const int row0 = tt * BT;
+  const int H = a.H;
+
+  const uint16_t* __restrict__ Wt = a.W + (tile_start - a.w_row0) * (int64_t)H;
+  const uint16_t* __restrict__ Ht = a.hidden + (int64_t)row0 * H;
+  const int rows_here = min(BT, a.rows - row0);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wv = wave % VW;
+  const int wt = wave / VW;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+
+  // Global element offsets of this thread's pieces (rows clamped into the valid range; the
+  // values loaded for clamped rows are never used).
+  int woff[WP], hoff[HP], wlds[WP], hlds[HP];
+#pragma unroll
+  for (int q = 0; q < WP; ++q) {
+    const int p = tid + NT * q, r = p >> 3, c = p & 7;
+    woff[q] = min(r, tile_len - 1) * H + c * 8;
+    wlds[q] = lds_off(r, c);
+  }
+#pragma unroll
+  for (int q = 0; q < HP; ++q) {
+    const int p = tid + NT * q, r = p >> 3, c = p & 7;
+    hoff[q] = min(r, rows_here - 1) * H + c * 8;
+    hlds[q] = lds_off(r, c);
+  }
+
+  u32x4 wreg[WP], hreg[HP];
+  auto gload = [&](int kc) {
+    const int k0 = kc * kKStage;
+#pragma unroll
+    for (int q = 0; q < WP; ++q) wreg[q] = *(const u32x4*)(Wt + woff[q] + k0);
+#pragma unroll
+    for (int q = 0; q < HP; ++q) hreg[q] = *(const u32x4*)(Ht + hoff[q] + k0);
+  };
+  auto lstore = [&](int st) {
+#pragma unroll
+    for (int q = 0; q < WP; ++q) *(u32x4*)(&lds_w[st][wlds[q]]) = wreg[q];
+#pragma unroll
+    for (int q = 0; q < HP; ++q) *(u32x4*)(&lds_h[st][hlds[q]]) = hreg[q];
+  };
+
+  f32x16 acc[VB][NTB];
+#pragma unroll
+  for (int i = 0; i < VB; ++i)
+#pragma unroll
+    for (int j = 0; j < NTB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // fragment row byte offsets (chunk added per MFMA step)
+  int arow[VB], brow[NTB];
+#pragma unroll
+  for (int i = 0; i < VB; ++i) arow[i] = (32 * (wv * VB + i) + col) * kRowBytes;
+#pragma unroll
+  for (int j = 0; j < NTB; ++j) brow[j] = (32 * (wt * NTB + j) + col) * kRowBytes;
+  const int sw = lane & 7;  // == fragment row & 7
+
+  const int nk = H / kKStage;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kc = 0; kc < nk; ++kc) {
+    const int st = kc & 1;
+    if (kc + 1 < nk) gload(kc + 1);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int cb = ((2 * s + half) ^ sw) << 4;
+      bf16x8 af[VB], bfr[NTB];
+#pragma unroll
+      for (int i = 0; i < VB; ++i) af[i] = *(const bf16x8*)(&lds_w[st][arow[i] + cb]);
+#pragma unroll
+      for (int j = 0; j < NTB; ++j) bfr[j] = *(const bf16x8*)(&lds_h[st][brow[j] + cb]);
+#pragma unroll
+      for (int i = 0; i < VB; ++i)
+#pragma unroll
+        for (int j = 0; j < NTB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    if (kc + 1 < nk) lstore(st ^ 1);
+    __syncthreads();
+  }
+
+  // ---------------------------------- epilogue ----------------------------------
+  if constexpr (TEMP) {
+#pragma unroll
+    for (int i = 0; i < VB; ++i)
+#pragma unroll
+      for (int j = 0; j < NTB; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = acc[i][j][r] * a.inv_tau;
+  }
+  const bool partial = tile_len < kVocabTile;
+  // column offset inside the tile of (block i, register r) for this lane
+  auto coff = [&](int i, int r) { return 32 * (wv * VB + i) + 8 * (r >> 2) + 4 * half + (r & 3); };
+
+  float m[NTB];
+#pragma unroll
+  for (int j = 0; j < NTB; ++j) {
+    float mm = -INFINITY;
+    if (partial) {
+#pragma unroll
+      for (int i = 0; i < VB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (coff(i, r) < tile_len) mm = fmaxf(mm, acc[i][j][r]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < VB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mm = fmaxf(mm, acc[i][j][r]);
+    }
+    m[j] = fmaxf(mm, __shfl_xor(mm, 32));
+  }
+  if constexpr (VW > 1) {
+#pragma unroll
+    for (int j = 0; j < NTB; ++j)
+      if (half == 0) red_m[wv][32 * (wt * NTB + j) + col] = m[j];
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NTB; ++j) {
+      float mm = red_m[0][32 * (wt * NTB + j) + col];
+#pragma unroll
+      for (int w = 1; w < VW; ++w) mm = fmaxf(mm, red_m[w][32 * (wt * NTB + j) + col]);
+      m[j] = mm;
+    }
+  }
+
+  float qs[NTB], qu[NTB];
+#pragma unroll
+  for (int j = 0; j < NTB; ++j) {
+    float p[VB], pu[VB];
+#pragma unroll
+    for (int i = 0; i < VB; ++i) {
+      float ps = 0.0f, pq = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float d = acc[i][j][r] - m[j];
+        float e = c_exp(d);
+        if (partial && coff(i, r) >= tile_len) e = 0.0f;
+        ps = ps + e;
+        if constexpr (ENT) {
+          float t = e * d;
+          if (partial && coff(i, r) >= tile_len) t = 0.0f;
+          pq = pq + t;
+        }
+      }
+      p[i] = ps;
+      pu[i] = pq;
+    }
+    qs[j] = tree_sum<VB>(p);
+    if constexpr (ENT) qu[j] = tree_sum<VB>(pu);
+  }
+
+  if constexpr (VW > 1) {
+#pragma unroll
+    for (int j = 0; j < NTB; ++j) {
+      red_s[wv][half][32 * (wt * NTB + j) + col] = qs[j];
+      if constexpr (ENT) red_u[wv][half][32 * (wt * NTB + j) + col] = qu[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NTB; ++j) {
+      float v[VW], vu[VW];
+#pragma unroll
+      for (int w = 0; w < VW; ++w) {
+        v[w] = red_s[w][half][32 * (wt * NTB + j) + col];
+        if constexpr (ENT) vu[w] = red_u[w][half][32 * (wt * NTB + j) + col];
+      }
+      qs[j] = tree_sum<VW>(v);
+      if constexpr (ENT) qu[j] = tree_sum<VW>(vu);
+    }
+  }
+
+  // halves: s = P[0] + P[1] (fp32 addition is commutative, so both lanes agree)
+  float* __restrict__ pm = a.part_m + (int64_t)(gtile - a.g_base) * a.ld;
+  float* __restrict__ psum = a.part_s + (int64_t)(gtile - a.g_base) * a.ld;
+#pragma unroll
+  for (int j = 0; j < NTB; ++j) {
+    const float s = qs[j] + __shfl_xor(qs[j], 32);
+    float u = 0.0f;
+    if constexpr (ENT) u = qu[j] + __shfl_xor(qu[j], 32);
+    const int rr = 32 * (wt * NTB + j) + col;  // row inside the row tile
+    if (wv == 0 && half == 0 && rr < rows_here) {
+      const int64_t t = (int64_t)row0 + rr;
+      pm[t] = m[j];
+      psum[t] = s;
+      if constexpr (ENT) a.part_u[(int64_t)(gtile - a.g_base) * a.ld + t] = u;
+    }
+  }
+
+  // target ownership: the lane whose registers hold column y_t of this tile writes z'[t, y_t]
+#pragma unroll
+  for (int j = 0; j < NTB; ++j) {
+    const int rr = 32 * (wt * NTB + j) + col;
+    int y = -1;
+    if (rr < rows_here) y = a.targets[row0 + rr];
+    const int64_t d = (int64_t)y - tile_start;
+    const bool in_tile = y >= 0 && d >= 0 && d < tile_len;
+    const int dd = (int)d;
+    const bool mine = in_tile && ((dd >> 5) / VB == wv) && (((dd >> 2) & 1) == half);
+    if (__any(mine)) {
+      const int ridx = ((dd >> 5) % VB) * 16 + ((dd >> 3) & 3) * 4 + (dd & 3);
+      float v = 0.0f;
+#pragma unroll
+      for (int i = 0; i < VB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v = (i * 16 + r == ridx) ? acc[i][j][r] : v;
+      if (mine) a.tgt[row0 + rr] = v;
+    }
+  }
+}
+
+// --------------------------------------------------------------------------------------------
+// K2a: per (row, segment) fold of the segment's tile partials (C8).
+// --------------------------------------------------------------------------------------------
+template <bool ENT>
+__global__ void __launch_bounds__(256) k_segment_fold(const FoldArgs a) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= a.rows) return;
+  const int sl = blockIdx.y;
+  const int seg = a.seg_begin + sl;
+  const int64_t g0 = (int64_t)seg * a.tiles_per_seg - a.g_base;
+  float M = -INFINITY;
+  for (int j = 0; j < a.tiles_per_seg; ++j) M = fmaxf(M, a.part_m[(g0 + j) * a.ld + t]);
+  float S = 0.0f, U = 0.0f;
+  for (int j = 0; j < a.tiles_per_seg; ++j) {
+    const int64_t o = (g0 + j) * a.ld + t;
+    const float mj = a.part_m[o];
+    const float sj = a.part_s[o];
+    const float dm = mj - M;
+    const float e = c_exp(dm);
+    S = S + sj * e;
+    if constexpr (ENT) U = U + (a.part_u[o] + sj * dm) * e;
+  }
+  const int32_t y = a.targets[t];
+  const int64_t lo = (int64_t)seg * a.seg_len;
+  const bool owner = y >= 0 && (int64_t)y >= lo && (int64_t)y < lo + a.seg_len;
+  rlk_segment_record_t r;
+  r.m = M;
+  r.s = S;
+  r.u = ENT ? U : 0.0f;
+  r.tgt = owner ? a.tgt[t] : __builtin_nanf("");
+  a.rec[(int64_t)sl * a.rec_ld + t] = r;
+}
+
+// --------------------------------------------------------------------------------------------
+// K2b: per row cross-segment merge and outputs (C9, C10).
+// --------------------------------------------------------------------------------------------
+template <int NS, bool ENT>
+__device__ __forceinline__ void merge_row(const MergeArgs& a, int t, int32_t y) {
+  float Ms[NS], Ss[NS], Us[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const rlk_segment_record_t r = a.rec[(int64_t)s * a.rec_ld + t];
+    Ms[s] = r.m;
+    Ss[s] = r.s;
+    Us[s] = r.u;
+  }
+  float M = Ms[0];
+#pragma unroll
+  for (int s = 1; s < NS; ++s) M = fmaxf(M, Ms[s]);
+  float as[NS], au[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const float dm = Ms[s] - M;
+    const float e = c_exp(dm);
+    as[s] = Ss[s] * e;
+    if constexpr (ENT) au[s] = (Us[s] + Ss[s] * dm) * e;
+  }
+  const float S = tree_sum<NS>(as);
+  const float logS = c_log(S);
+  const float lse = M + logS;
+  const int owner = (int)((int64_t)y / a.seg_len);
+  const float zy = a.rec[(int64_t)owner * a.rec_ld + t].tgt;
+  a.logp[t] = zy - lse;
+  a.lse[t] = lse;
+  if constexpr (ENT) {
+    const float U = tree_sum<NS>(au);
+    a.entropy[t] = logS - U / S;
+  }
+}
+
+template <bool ENT>
+__global__ void __launch_bounds__(256) k_merge(const MergeArgs a) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= a.rows) return;
+  const int32_t y = a.targets[t];
+  if (y < 0) {
+    a.logp[t] = 0.0f;
+    a.lse[t] = 0.0f;
+    if constexpr (ENT) a.entropy[t] = 0.0f;
+    return;
+  }
+  if ((int64_t)y >= a.vocab) {
+    const float nan = __builtin_nanf("");
+    a.logp[t] = nan;
+    a.lse[t] = nan;
+    if constexpr (ENT) a.entropy[t] = nan;
+    if (a.status) atomicOr(a.status, (unsigned)RLK_DEVICE_STATUS_BAD_TARGET);
+    return;
+  }
+  switch (a.n_seg) {
+    case 1: merge_row<1, ENT>(a, t, y); break;
+    case 2: merge_row<2, ENT>(a, t, y); break;
+    case 4: merge_row<4, ENT>(a, t, y); break;
+    default: merge_row<8, ENT>(a, t, y); break;
+  }
+}
+
+// --------------------------------------------------------------------------------------------
+// K0: final RMSNorm, one 64-wide wave per row (C12).
+// --------------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) k_rmsnorm(const RmsArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.rows) return;
+  const uint16_t* __restrict__ x = a.x + (int64_t)row * a.H;
+  uint16_t* __restrict__ y = a.y + (int64_t)row * a.H;
+  const int npieces = a.H / 8;
+  float ss = 0.0f;
+  for (int p = lane; p < npieces; p += 64) {
+    const u32x4 v = *(const u32x4*)(x + p * 8);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float lo = bf16_to_f32(v[w] & 0xffffu);
+      const float hi = bf16_to_f32(v[w] >> 16);
+      ss = ss + lo * lo;
+      ss = ss + hi * hi;
+    }
+  }
+  ss = ss + __shfl_xor(ss, 32);
+  ss = ss + __shfl_xor(ss, 16);
+  ss = ss + __shfl_xor(ss, 8);
+  ss = ss + __shfl_xor(ss, 4);
+  ss = ss + __shfl_xor(ss, 2);
+  ss = ss + __shfl_xor(ss, 1);
+  const float r = c_rsq(ss * a.inv_H + a.eps);
+  for (int p = lane; p < npieces; p += 64) {
+    const u32x4 v = *(const u32x4*)(x + p * 8);
+    const u32x4 g = *(const u32x4*)(a.gamma + p * 8);
+    u32x4 o;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float lo = (bf16_to_f32(v[w] & 0xffffu) * r) * bf16_to_f32(g[w] & 0xffffu);
+      const float hi = (bf16_to_f32(v[w] >> 16) * r) * bf16_to_f32(g[w] >> 16);
+      o[w] = (uint32_t)bf16_rne(lo) | ((uint32_t)bf16_rne(hi) << 16);
+    }
+    *(u32x4*)(y + p * 8) = o;
+  }
+}
+
+__global__ void k_clear_status(uint32_t* status) {
+  if (threadIdx.x == 0) *status = 0u;
+}
+
+// --------------------------------------------------------------------------------------------
+// launchers
+// --------------------------------------------------------------------------------------------
+bool token_tile_supported(int bt) { return bt == 32 || bt == 64 || bt == 128 || bt == 256; }
+
+template <int VW, int TW, int NTB>
+static hipError_t launch_variant(const LmheadArgs& a, bool ent, hipStream_t s) {
+  constexpr int BT = 32 * NTB * TW;
+  const int64_t n_vt = (int64_t)a.n_seg * a.tiles_per_seg;
+  const int64_t n_tt = (a.rows + BT - 1) / BT;
+  const int64_t items = n_vt * n_tt;
+  const int64_t blocks = (items + 7) / 8 * 8;
+  if (items == 0) return hipSuccess;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)blocks), block(64 * VW * TW);
+  const bool temp = a.inv_tau != 1.0f;
+  if (ent) {
+    if (temp) hipLaunchKernelGGL((k_lmhead<VW, TW, NTB, true, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_lmhead<VW, TW, NTB, true, false>), grid, block, 0, s, a);
+  } else {
+    if (temp) hipLaunchKernelGGL((k_lmhead<VW, TW, NTB, false, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_lmhead<VW, TW, NTB, false, false>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_lmhead(const LmheadArgs& a, int bt, bool ent, hipStream_t s) {
+  switch (bt) {
+    case 256: return launch_variant<1, 4, 2>(a, ent, s);
+    case 128: return launch_variant<2, 2, 2>(a, ent, s);
+    case 64: return launch_variant<4, 1, 2>(a, ent, s);
+    case 32: return launch_variant<4, 1, 1>(a, ent, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_fold(const FoldArgs& a, bool ent, hipStream_t s) {
+  if (a.rows == 0 || a.n_seg == 0) return hipSuccess;
+  const dim3 grid((unsigned)((a.rows + 255) / 256), (unsigned)a.n_seg), block(256);
+  if (ent) hipLaunchKernelGGL(k_segment_fold<true>, grid, block, 0, s, a);
+  else hipLaunchKernelGGL(k_segment_fold<false>, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const MergeArgs& a, bool ent, hipStream_t s) {
+  if (a.rows == 0) return hipSuccess;
+  const dim3 grid((unsigned)((a.rows + 255) / 256)), block(256);
+  if (ent) hipLaunchKernelGGL(k_merge<true>, grid, block, 0, s, a);
+  else hipLaunchKernelGGL(k_merge<false>, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(const RmsArgs& a, hipStream_t s) {
+  if (a.rows == 0) return hipSuccess;
+  const dim3 grid((unsigned)((a.rows + 3) / 4)), block(256);
+  hipLaunchKernelGGL(k_rmsnorm, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_clear_status(uint32_t* status, hipStream_t s) {
+  hipLaunchKernelGGL(k_clear_status, dim3(1), dim3(64), 0, s, status);
+  return hipGetLastError();
+}
+
+}  // namespace rlk
