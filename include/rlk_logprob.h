@@ -133,6 +133,17 @@ rlk_status_t rlk_logprob_forward(rlk_logprob_t handle, const void* hidden, const
                                  const void* rms_gamma, float* logp, float* lse, float* entropy,
                                  void* workspace, size_t workspace_bytes, rlk_stream_t stream);
 
+/* rlk_logprob_forward that also records caller-created HIP events (hipEvent_t) on `stream`:
+ * events[2i] right before and events[2i+1] right after the i-th LM-head kernel launch, for
+ * i < num_events / 2 (extra launches are not bracketed). For measuring that kernel's duration
+ * with the caller's clock; the results are bit-identical to rlk_logprob_forward. */
+rlk_status_t rlk_logprob_forward_timed(rlk_logprob_t handle, const void* hidden, const void* W_lm,
+                                       const int32_t* targets, const rlk_layout_desc_t* layout,
+                                       const void* rms_gamma, float* logp, float* lse,
+                                       float* entropy, void* workspace, size_t workspace_bytes,
+                                       rlk_stream_t stream, void* const* events,
+                                       int32_t num_events);
+
 /* Host-only: workspace bytes of rlk_logprob_partials for `num_rows` rows over the vocab range
  * [vocab_begin, vocab_end). */
 rlk_status_t rlk_logprob_partials_workspace_size(const rlk_logprob_config_t* config,

@@ -74,6 +74,9 @@ _SIGS = {
                                ctypes.POINTER(rlk_layout_desc_t), ctypes.POINTER(ctypes.c_int64)]),
     "rlk_logprob_forward": (_ST, [_H, _P, _P, _P, ctypes.POINTER(rlk_layout_desc_t), _P, _P, _P,
                                   _P, _P, ctypes.c_size_t, _S]),
+    "rlk_logprob_forward_timed": (_ST, [_H, _P, _P, _P, ctypes.POINTER(rlk_layout_desc_t), _P, _P,
+                                        _P, _P, _P, ctypes.c_size_t, _S,
+                                        ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]),
     "rlk_logprob_partials_workspace_size": (_ST, [ctypes.POINTER(rlk_logprob_config_t),
                                                   ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                                   ctypes.POINTER(ctypes.c_size_t)]),
@@ -159,6 +162,16 @@ def rlk_logprob_forward(handle, hidden, W_lm, targets, layout, rms_gamma, logp, 
     check(load().rlk_logprob_forward(handle, hidden, W_lm, targets, ctypes.byref(layout),
                                      rms_gamma, logp, lse, entropy, workspace, workspace_bytes,
                                      stream), "rlk_logprob_forward")
+
+
+def rlk_logprob_forward_timed(handle, hidden, W_lm, targets, layout, rms_gamma, logp, lse,
+                              entropy, workspace, workspace_bytes, stream, events) -> None:
+    """events: a sequence of hipEvent_t integers (2 per LM-head launch to bracket)."""
+    arr = (ctypes.c_void_p * max(1, len(events)))(*events)
+    check(load().rlk_logprob_forward_timed(handle, hidden, W_lm, targets, ctypes.byref(layout),
+                                           rms_gamma, logp, lse, entropy, workspace,
+                                           workspace_bytes, stream, arr, len(events)),
+          "rlk_logprob_forward_timed")
 
 
 def rlk_logprob_partials_workspace_size(config, num_rows, vocab_begin, vocab_end) -> int:

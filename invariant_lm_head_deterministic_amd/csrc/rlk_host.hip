@@ -352,11 +352,12 @@ RLK_API rlk_status_t rlk_logprob_workspace_size(const rlk_logprob_config_t* conf
   return ok();
 }
 
-RLK_API rlk_status_t rlk_logprob_forward(rlk_logprob_t h, const void* hidden, const void* W_lm,
-                                         const int32_t* targets, const rlk_layout_desc_t* layout,
-                                         const void* rms_gamma, float* logp, float* lse,
-                                         float* entropy, void* workspace, size_t workspace_bytes,
-                                         rlk_stream_t stream) {
+namespace {
+rlk_status_t forward_impl(rlk_logprob_t h, const void* hidden, const void* W_lm,
+                          const int32_t* targets, const rlk_layout_desc_t* layout,
+                          const void* rms_gamma, float* logp, float* lse, float* entropy,
+                          void* workspace, size_t workspace_bytes, rlk_stream_t stream,
+                          void* const* events, int32_t num_events) {
   if (!h) return fail(RLK_ERR_INVALID_ARGUMENT, "handle is NULL");
   const rlk_logprob_config_t& c = h->cfg;
   Plan p;
@@ -393,15 +394,26 @@ RLK_API rlk_status_t rlk_logprob_forward(rlk_logprob_t h, const void* hidden, co
 
   const int seg_per_shard = c.vocab_segments / p.shards;
   const int64_t H = c.hidden_size;
+  int64_t launch_no = 0;
   for (size_t b = 0; b < p.batches.size(); ++b) {
     for (const RowRange& ch : p.chunks[b]) {
       for (int sh = 0; sh < p.shards; ++sh) {
         const int s0 = sh * seg_per_shard, s1 = s0 + seg_per_shard;
         const int64_t w_row0 = (int64_t)s0 * g.seg_len;
         const void* Wsh = static_cast<const uint16_t*>(W_lm) + w_row0 * H;
+        const bool timed = events && 2 * launch_no + 1 < (int64_t)num_events;
+        if (timed) {
+          e = hipEventRecord(static_cast<hipEvent_t>(events[2 * launch_no]), s);
+          if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+        }
         st = run_rows(h, g, hidden, Wsh, w_row0, targets, rms_gamma, m, ws, T, 0, ch.begin,
                       ch.end, s0, s1, layout->token_tile, sh == 0, s);
         if (st != RLK_OK) return st;
+        if (timed) {
+          e = hipEventRecord(static_cast<hipEvent_t>(events[2 * launch_no + 1]), s);
+          if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+        }
+        ++launch_no;
       }
     }
     const RowRange& br = p.batches[b];
@@ -440,6 +452,30 @@ RLK_API rlk_status_t rlk_logprob_forward(rlk_logprob_t h, const void* hidden, co
     if (e != hipSuccess) return hip_fail(e, "merge launch");
   }
   return ok();
+}
+
+}  // namespace
+
+RLK_API rlk_status_t rlk_logprob_forward(rlk_logprob_t h, const void* hidden, const void* W_lm,
+                                         const int32_t* targets, const rlk_layout_desc_t* layout,
+                                         const void* rms_gamma, float* logp, float* lse,
+                                         float* entropy, void* workspace, size_t workspace_bytes,
+                                         rlk_stream_t stream) {
+  return forward_impl(h, hidden, W_lm, targets, layout, rms_gamma, logp, lse, entropy, workspace,
+                      workspace_bytes, stream, nullptr, 0);
+}
+
+RLK_API rlk_status_t rlk_logprob_forward_timed(rlk_logprob_t h, const void* hidden,
+                                               const void* W_lm, const int32_t* targets,
+                                               const rlk_layout_desc_t* layout,
+                                               const void* rms_gamma, float* logp, float* lse,
+                                               float* entropy, void* workspace,
+                                               size_t workspace_bytes, rlk_stream_t stream,
+                                               void* const* events, int32_t num_events) {
+  if (num_events < 0 || (num_events > 0 && !events))
+    return fail(RLK_ERR_INVALID_ARGUMENT, "events must hold num_events >= 0 entries");
+  return forward_impl(h, hidden, W_lm, targets, layout, rms_gamma, logp, lse, entropy, workspace,
+                      workspace_bytes, stream, events, num_events);
 }
 
 RLK_API rlk_status_t rlk_logprob_partials_workspace_size(const rlk_logprob_config_t* config,

@@ -360,22 +360,46 @@ k_lmhead(const LmheadArgs a) {
 // --------------------------------------------------------------------------------------------
 template <bool ENT>
 __global__ void __launch_bounds__(256) k_segment_fold(const FoldArgs a) {
+  // The fold is one sequential chain per (row, segment) by contract; its loads do not depend on
+  // the chain, so they are issued in batches of U ahead of the arithmetic.
+  constexpr int U = 16;
   const int t = blockIdx.x * 256 + threadIdx.x;
   if (t >= a.rows) return;
   const int sl = blockIdx.y;
   const int seg = a.seg_begin + sl;
   const int64_t g0 = (int64_t)seg * a.tiles_per_seg - a.g_base;
+  const float* __restrict__ pm = a.part_m + g0 * a.ld + t;
+  const float* __restrict__ ps = a.part_s + g0 * a.ld + t;
+  const float* __restrict__ pu = ENT ? a.part_u + g0 * a.ld + t : nullptr;
+  const int n = a.tiles_per_seg;
   float M = -INFINITY;
-  for (int j = 0; j < a.tiles_per_seg; ++j) M = fmaxf(M, a.part_m[(g0 + j) * a.ld + t]);
-  float S = 0.0f, U = 0.0f;
-  for (int j = 0; j < a.tiles_per_seg; ++j) {
-    const int64_t o = (g0 + j) * a.ld + t;
-    const float mj = a.part_m[o];
-    const float sj = a.part_s[o];
-    const float dm = mj - M;
-    const float e = c_exp(dm);
-    S = S + sj * e;
-    if constexpr (ENT) U = U + (a.part_u[o] + sj * dm) * e;
+  for (int j0 = 0; j0 < n; j0 += U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = (j0 + u < n) ? pm[(int64_t)(j0 + u) * a.ld] : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) M = fmaxf(M, v[u]);
+  }
+  float S = 0.0f, U_ = 0.0f;
+  for (int j0 = 0; j0 < n; j0 += U) {
+    float vm[U], vs[U], vu[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool in = j0 + u < n;
+      const int64_t o = (int64_t)(j0 + u) * a.ld;
+      vm[u] = in ? pm[o] : 0.0f;
+      vs[u] = in ? ps[o] : 0.0f;
+      if constexpr (ENT) vu[u] = in ? pu[o] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (j0 + u < n) {
+        const float dm = vm[u] - M;
+        const float e = c_exp(dm);
+        S = S + vs[u] * e;
+        if constexpr (ENT) U_ = U_ + (vu[u] + vs[u] * dm) * e;
+      }
+    }
   }
   const int32_t y = a.targets[t];
   const int64_t lo = (int64_t)seg * a.seg_len;
@@ -383,7 +407,7 @@ __global__ void __launch_bounds__(256) k_segment_fold(const FoldArgs a) {
   rlk_segment_record_t r;
   r.m = M;
   r.s = S;
-  r.u = ENT ? U : 0.0f;
+  r.u = ENT ? U_ : 0.0f;
   r.tgt = owner ? a.tgt[t] : __builtin_nanf("");
   a.rec[(int64_t)sl * a.rec_ld + t] = r;
 }
