@@ -75,9 +75,20 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
-// Byte offset of 16-byte piece c (0..7) of staged row `row`: pieces are XOR-swizzled by the
-// row's low 3 bits so that the 8 rows read together by a fragment load hit distinct banks.
-__device__ __forceinline__ int lds_off(int row, int c) { return row * kRowBytes + ((c ^ (row & 7)) << 4); }
+// Staged tiles hold rows of 128 bytes (64 bf16 of K) as 8 pieces of 16 bytes. Piece c of row r
+// sits at position c ^ ((r >> 1) & 7): a fragment read of 16 consecutive rows (one pass of a
+// 16-byte-per-lane LDS read over 64 banks) then touches every bank exactly once.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
+typedef __attribute__((address_space(1))) const void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
+
+// Asynchronous 16-byte-per-lane copy global -> LDS; lane l's bytes land at lds_base + 16 l.
+__device__ __forceinline__ void dma16(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((gptr_t)g, (lptr_t)lds_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_dma() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Balanced pairwise sum of N = 2^k values in index order (the C5/C9 tree).
 template <int N>
@@ -106,12 +117,17 @@ k_lmhead(const LmheadArgs a) {
   constexpr int NT = 64 * NWAVES;
   constexpr int BT = 32 * NTB * TW;
   constexpr int VB = 8 / VW;
-  constexpr int WP = kVocabTile * 8 / NT;  // 16-byte pieces of a W stage per thread
-  constexpr int HP = BT * 8 / NT;          // 16-byte pieces of a hidden stage per thread
-  static_assert(VB * VW == 8 && WP * NT == kVocabTile * 8 && HP * NT == BT * 8, "tiling");
+  constexpr int WI = kVocabTile / 8 / NWAVES;  // DMA instructions per wave per W stage
+  constexpr int HI = BT / 8 / NWAVES;          // DMA instructions per wave per hidden stage
+  static_assert(VB * VW == 8 && WI * 8 * NWAVES == kVocabTile && HI * 8 * NWAVES == BT, "tiling");
+  (void)NT;
 
-  __shared__ __attribute__((aligned(16))) uint8_t lds_w[2][kVocabTile * kRowBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_h[2][BT * kRowBytes];
+  // two stages as distinct objects, so the compiler can tell a DMA into one stage from reads
+  // of the other and does not wait for the DMA before those reads
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_w0[kVocabTile * kRowBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_w1[kVocabTile * kRowBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_h0[BT * kRowBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_h1[BT * kRowBytes];
   __shared__ float red_m[VW > 1 ? VW : 1][BT];
   __shared__ float red_s[VW > 1 ? VW : 1][2][BT];
   __shared__ float red_u[(VW > 1 && ENT) ? VW : 1][2][BT];
@@ -153,35 +169,30 @@ k_lmhead(const LmheadArgs a) {
   const int half = lane >> 5;
   const int col = lane & 31;
 
-  // Global element offsets of this thread's pieces (rows clamped into the valid range; the
-  // values loaded for clamped rows are never used).
-  int woff[WP], hoff[HP], wlds[WP], hlds[HP];
+  // Direct-to-LDS staging: DMA instruction q of this wave fills the 8 staged rows starting at
+  // 8 (q * NWAVES + wave); lane l writes position l & 7 of row (l >> 3) of that group, so it
+  // loads the logical piece that the swizzle puts there. Rows past the tile or the launch are
+  // clamped to the last valid row (their results are never used).
+  int wgo[WI], hgo[HI];
 #pragma unroll
-  for (int q = 0; q < WP; ++q) {
-    const int p = tid + NT * q, r = p >> 3, c = p & 7;
-    woff[q] = min(r, tile_len - 1) * H + c * 8;
-    wlds[q] = lds_off(r, c);
+  for (int q = 0; q < WI; ++q) {
+    const int r = 8 * (q * NWAVES + wave) + (lane >> 3);
+    const int c = (lane & 7) ^ swz(r);
+    wgo[q] = min(r, tile_len - 1) * H + c * 8;
   }
 #pragma unroll
-  for (int q = 0; q < HP; ++q) {
-    const int p = tid + NT * q, r = p >> 3, c = p & 7;
-    hoff[q] = min(r, rows_here - 1) * H + c * 8;
-    hlds[q] = lds_off(r, c);
+  for (int q = 0; q < HI; ++q) {
+    const int r = 8 * (q * NWAVES + wave) + (lane >> 3);
+    const int c = (lane & 7) ^ swz(r);
+    hgo[q] = min(r, rows_here - 1) * H + c * 8;
   }
-
-  u32x4 wreg[WP], hreg[HP];
-  auto gload = [&](int kc) {
-    const int k0 = kc * kKStage;
+  auto issue = [&](int kc, uint8_t* lw, uint8_t* lh) {
+    const uint16_t* wb = Wt + kc * kKStage;
+    const uint16_t* hb = Ht + kc * kKStage;
 #pragma unroll
-    for (int q = 0; q < WP; ++q) wreg[q] = *(const u32x4*)(Wt + woff[q] + k0);
+    for (int q = 0; q < WI; ++q) dma16(wb + wgo[q], lw + 8 * (q * NWAVES + wave) * kRowBytes);
 #pragma unroll
-    for (int q = 0; q < HP; ++q) hreg[q] = *(const u32x4*)(Ht + hoff[q] + k0);
-  };
-  auto lstore = [&](int st) {
-#pragma unroll
-    for (int q = 0; q < WP; ++q) *(u32x4*)(&lds_w[st][wlds[q]]) = wreg[q];
-#pragma unroll
-    for (int q = 0; q < HP; ++q) *(u32x4*)(&lds_h[st][hlds[q]]) = hreg[q];
+    for (int q = 0; q < HI; ++q) dma16(hb + hgo[q], lh + 8 * (q * NWAVES + wave) * kRowBytes);
   };
 
   f32x16 acc[VB][NTB];
@@ -192,38 +203,71 @@ k_lmhead(const LmheadArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // fragment row byte offsets (chunk added per MFMA step)
+  // fragment row byte offsets; every fragment row has (row >> 1) & 7 == (col >> 1) & 7
   int arow[VB], brow[NTB];
 #pragma unroll
   for (int i = 0; i < VB; ++i) arow[i] = (32 * (wv * VB + i) + col) * kRowBytes;
 #pragma unroll
   for (int j = 0; j < NTB; ++j) brow[j] = (32 * (wt * NTB + j) + col) * kRowBytes;
-  const int sw = lane & 7;  // == fragment row & 7
+  const int sw = swz(col);
 
-  const int nk = H / kKStage;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kc = 0; kc < nk; ++kc) {
-    const int st = kc & 1;
-    if (kc + 1 < nk) gload(kc + 1);
+  bf16x8 fa[2][VB], fb[2][NTB];
+  auto load_frags = [&](const uint8_t* lw, const uint8_t* lh, int s, int buf) {
+    const int cb = ((2 * s + half) ^ sw) << 4;
+#pragma unroll
+    for (int i = 0; i < VB; ++i) fa[buf][i] = *(const bf16x8*)(lw + arow[i] + cb);
+#pragma unroll
+    for (int j = 0; j < NTB; ++j) fb[buf][j] = *(const bf16x8*)(lh + brow[j] + cb);
+  };
+
+  // One K stage: DMA of stage kc+1 into (nw, nh) while the 4 MFMA sub-steps of stage kc run
+  // from (cw, ch); then wait for this wave's DMA and meet the other waves at the barrier.
+  auto stage = [&](int kc, int nk, const uint8_t* cw, const uint8_t* ch, uint8_t* nw,
+                   uint8_t* nh) {
+    if (kc + 1 < nk) issue(kc + 1, nw, nh);
+    load_frags(cw, ch, 0, 0);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int cb = ((2 * s + half) ^ sw) << 4;
-      bf16x8 af[VB], bfr[NTB];
-#pragma unroll
-      for (int i = 0; i < VB; ++i) af[i] = *(const bf16x8*)(&lds_w[st][arow[i] + cb]);
-#pragma unroll
-      for (int j = 0; j < NTB; ++j) bfr[j] = *(const bf16x8*)(&lds_h[st][brow[j] + cb]);
+      if (s + 1 < 4) load_frags(cw, ch, s + 1, (s + 1) & 1);
 #pragma unroll
       for (int i = 0; i < VB; ++i)
 #pragma unroll
         for (int j = 0; j < NTB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s & 1][i], fb[s & 1][j],
+                                                              acc[i][j], 0, 0, 0);
     }
-    if (kc + 1 < nk) lstore(st ^ 1);
+    // Schedule: the next stage's DMA and this stage's first fragments up front, then each
+    // sub-step's MFMAs with the following sub-step's fragment reads threaded between them.
+    constexpr int NF = VB + NTB;  // fragment reads per sub-step
+    constexpr int NM = VB * NTB;  // MFMAs per sub-step
+    constexpr int NI = NF < NM ? NF : NM;
+    __builtin_amdgcn_sched_group_barrier(0x020, WI + HI, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, NF, 0);
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      if constexpr (NF > NI) __builtin_amdgcn_sched_group_barrier(0x100, NF - NI, 0);
+      if constexpr (NM > NI) __builtin_amdgcn_sched_group_barrier(0x008, NM - NI, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+    wait_dma();
     __syncthreads();
+  };
+
+  const int nk = H / kKStage;
+  issue(0, lds_w0, lds_h0);
+  wait_dma();
+  __syncthreads();
+  int kc = 0;
+  for (; kc + 1 < nk; kc += 2) {
+    stage(kc, nk, lds_w0, lds_h0, lds_w1, lds_h1);
+    stage(kc + 1, nk, lds_w1, lds_h1, lds_w0, lds_h0);
   }
+  if (kc < nk) stage(kc, nk, lds_w0, lds_h0, lds_w1, lds_h1);
 
   // ---------------------------------- epilogue ----------------------------------
   if constexpr (TEMP) {
