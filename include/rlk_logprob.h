@@ -62,7 +62,7 @@ typedef enum rlk_status {
   RLK_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, inconsistent layout */
   RLK_ERR_NO_DEVICE = 2,        /* no HIP device, or the device index does not exist */
   RLK_ERR_UNSUPPORTED_ARCH = 3, /* device is not gfx950 */
-  RLK_ERR_UNSUPPORTED_SHAPE = 4,/* H not a multiple of 64, V not a multiple of the segments ... */
+  RLK_ERR_UNSUPPORTED_SHAPE = 4,/* H not a multiple of 128, V not a multiple of the segments ... */
   RLK_ERR_ALIGNMENT = 5,        /* a device pointer is not 16-byte aligned */
   RLK_ERR_WORKSPACE = 6,        /* workspace missing or smaller than the size query returned */
   RLK_ERR_CONTRACT = 7,         /* shard range not on segment boundaries, flags mismatch */
@@ -78,7 +78,7 @@ typedef enum rlk_status {
 
 /* Numeric configuration, fixed at creation. Every field is part of the contract id. */
 typedef struct rlk_logprob_config {
-  int32_t hidden_size;     /* H: a multiple of 64, at most 65536 */
+  int32_t hidden_size;     /* H: a multiple of 128, at most 65536 */
   int32_t vocab_segments;  /* S_c: 1, 2, 4 or 8 contiguous vocab segments (contract split) */
   int64_t vocab_size;      /* V: a multiple of S_c; V / S_c at most 2^24 */
   float inv_temperature;   /* fl32(1/tau) multiplied into every logit; 1.0f = no temperature */

@@ -73,8 +73,8 @@ rlk_status_t check_config(const rlk_logprob_config_t* c) {
   if (c->reserved != 0) return fail(RLK_ERR_INVALID_ARGUMENT, "config.reserved must be 0");
   if (c->flags & ~(RLK_FLAG_RMSNORM | RLK_FLAG_ENTROPY))
     return fail(RLK_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", c->flags);
-  if (c->hidden_size <= 0 || c->hidden_size % 64 != 0 || c->hidden_size > 65536)
-    return fail(RLK_ERR_UNSUPPORTED_SHAPE, "hidden_size %d is not a positive multiple of 64 <= 65536",
+  if (c->hidden_size <= 0 || c->hidden_size % 128 != 0 || c->hidden_size > 65536)
+    return fail(RLK_ERR_UNSUPPORTED_SHAPE, "hidden_size %d is not a positive multiple of 128 <= 65536",
                 c->hidden_size);
   const int s = c->vocab_segments;
   if (s != 1 && s != 2 && s != 4 && s != 8)

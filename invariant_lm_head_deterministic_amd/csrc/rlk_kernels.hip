@@ -50,6 +50,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "rlk_internal.h"
 
 namespace rlk {
@@ -80,12 +82,19 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as
 // 16-byte-per-lane LDS read over 64 banks) then touches every bank exactly once.
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
-typedef __attribute__((address_space(1))) const void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 
-// Asynchronous 16-byte-per-lane copy global -> LDS; lane l's bytes land at lds_base + 16 l.
-__device__ __forceinline__ void dma16(const void* g, void* lds_base) {
-  __builtin_amdgcn_global_load_lds((gptr_t)g, (lptr_t)lds_base, 16, 0, 0);
+// Buffer descriptor over `bytes` bytes from `base` (raw, unstrided; the word-3 value selects
+// 32-bit data format, which makes the descriptor valid for untyped loads).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, 0x00020000);
+}
+
+// Asynchronous 16-byte-per-lane copy global -> LDS (buffer_load_dwordx4 ... lds): lane l's bytes
+// come from byte offset voff + soff of the descriptor and land at lds_base + 16 l.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds_base, uint32_t voff,
+                                      uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lptr_t)lds_base, 16, voff, soff, 0, 0);
 }
 
 __device__ __forceinline__ void wait_dma() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -163,7 +172,7 @@ k_lmhead(const LmheadArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wv = wave % VW;
   const int wt = wave / VW;
   const int half = lane >> 5;
@@ -172,27 +181,29 @@ k_lmhead(const LmheadArgs a) {
   // Direct-to-LDS staging: DMA instruction q of this wave fills the 8 staged rows starting at
   // 8 (q * NWAVES + wave); lane l writes position l & 7 of row (l >> 3) of that group, so it
   // loads the logical piece that the swizzle puts there. Rows past the tile or the launch are
-  // clamped to the last valid row (their results are never used).
-  int wgo[WI], hgo[HI];
+  // clamped to the last valid row (their results are never used), so every address lies inside
+  // the tile's descriptor. The per-lane byte offsets are fixed; the K stage is the scalar offset.
+  uint32_t wgo[WI], hgo[HI];
 #pragma unroll
   for (int q = 0; q < WI; ++q) {
     const int r = 8 * (q * NWAVES + wave) + (lane >> 3);
     const int c = (lane & 7) ^ swz(r);
-    wgo[q] = min(r, tile_len - 1) * H + c * 8;
+    wgo[q] = (uint32_t)(min(r, tile_len - 1) * H + c * 8) * 2u;
   }
 #pragma unroll
   for (int q = 0; q < HI; ++q) {
     const int r = 8 * (q * NWAVES + wave) + (lane >> 3);
     const int c = (lane & 7) ^ swz(r);
-    hgo[q] = min(r, rows_here - 1) * H + c * 8;
+    hgo[q] = (uint32_t)(min(r, rows_here - 1) * H + c * 8) * 2u;
   }
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(Wt, tile_len * H * 2);
+  const __amdgpu_buffer_rsrc_t rh = make_rsrc(Ht, rows_here * H * 2);
   auto issue = [&](int kc, uint8_t* lw, uint8_t* lh) {
-    const uint16_t* wb = Wt + kc * kKStage;
-    const uint16_t* hb = Ht + kc * kKStage;
+    const uint32_t so = (uint32_t)kc * kRowBytes;
 #pragma unroll
-    for (int q = 0; q < WI; ++q) dma16(wb + wgo[q], lw + 8 * (q * NWAVES + wave) * kRowBytes);
+    for (int q = 0; q < WI; ++q) dma16(rw, lw + 8 * (q * NWAVES + wave) * kRowBytes, wgo[q], so);
 #pragma unroll
-    for (int q = 0; q < HI; ++q) dma16(hb + hgo[q], lh + 8 * (q * NWAVES + wave) * kRowBytes);
+    for (int q = 0; q < HI; ++q) dma16(rh, lh + 8 * (q * NWAVES + wave) * kRowBytes, hgo[q], so);
   };
 
   f32x16 acc[VB][NTB];
@@ -203,71 +214,93 @@ k_lmhead(const LmheadArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // fragment row byte offsets; every fragment row has (row >> 1) & 7 == (col >> 1) & 7
-  int arow[VB], brow[NTB];
-#pragma unroll
-  for (int i = 0; i < VB; ++i) arow[i] = (32 * (wv * VB + i) + col) * kRowBytes;
-#pragma unroll
-  for (int j = 0; j < NTB; ++j) brow[j] = (32 * (wt * NTB + j) + col) * kRowBytes;
+  // Fragment reads: one lane offset per MFMA sub-step (every fragment row has the same
+  // (row >> 1) & 7 as col), the 32-row blocks at constant 4 KB strides.
   const int sw = swz(col);
-
+  int loff[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) loff[s] = col * kRowBytes + (((2 * s + half) ^ sw) << 4);
+  const int a0 = 32 * wv * VB * kRowBytes, b0 = 32 * wt * NTB * kRowBytes;
   bf16x8 fa[2][VB], fb[2][NTB];
   auto load_frags = [&](const uint8_t* lw, const uint8_t* lh, int s, int buf) {
-    const int cb = ((2 * s + half) ^ sw) << 4;
+    const uint8_t* pa = lw + a0 + loff[s];
+    const uint8_t* pb = lh + b0 + loff[s];
 #pragma unroll
-    for (int i = 0; i < VB; ++i) fa[buf][i] = *(const bf16x8*)(lw + arow[i] + cb);
+    for (int i = 0; i < VB; ++i) fa[buf][i] = *(const bf16x8*)(pa + i * 32 * kRowBytes);
 #pragma unroll
-    for (int j = 0; j < NTB; ++j) fb[buf][j] = *(const bf16x8*)(lh + brow[j] + cb);
+    for (int j = 0; j < NTB; ++j) fb[buf][j] = *(const bf16x8*)(pb + j * 32 * kRowBytes);
   };
+  auto mfmas = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < VB; ++i)
+#pragma unroll
+      for (int j = 0; j < NTB; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0,
+                                                            0, 0);
+  };
+  // Instruction order inside one sub-step: each MFMA followed by one fragment read for the
+  // next sub-step, DMA instructions spread evenly over the MFMAs.
+  constexpr int NF = VB + NTB;  // fragment reads per sub-step
+  constexpr int NM = VB * NTB;  // MFMAs per sub-step
+  auto sched_sub = [&](auto nreads_c, auto ndma_c) {
+    constexpr int NR = decltype(nreads_c)::value;
+    constexpr int ND = decltype(ndma_c)::value;
+    constexpr int NDs = ND > 0 ? ND : 1;
+    constexpr int EV = ND > 0 ? (NM / NDs > 0 ? NM / NDs : 1) : NM + 1;
+    constexpr int INLOOP = ND > 0 ? (NM / EV < ND ? NM / EV : ND) : 0;
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (ND > 0 && i % EV == EV - 1 && i / EV < INLOOP)
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+    if constexpr (ND > INLOOP) __builtin_amdgcn_sched_group_barrier(0x020, ND - INLOOP, 0);
+  };
+  using ICR = std::integral_constant<int, NF>;
+  using IC0 = std::integral_constant<int, 0>;
+  using ICD = std::integral_constant<int, WI + HI>;
 
-  // One K stage: DMA of stage kc+1 into (nw, nh) while the 4 MFMA sub-steps of stage kc run
-  // from (cw, ch); then wait for this wave's DMA and meet the other waves at the barrier.
-  auto stage = [&](int kc, int nk, const uint8_t* cw, const uint8_t* ch, uint8_t* nw,
-                   uint8_t* nh) {
-    if (kc + 1 < nk) issue(kc + 1, nw, nh);
-    load_frags(cw, ch, 0, 0);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      if (s + 1 < 4) load_frags(cw, ch, s + 1, (s + 1) & 1);
-#pragma unroll
-      for (int i = 0; i < VB; ++i)
-#pragma unroll
-        for (int j = 0; j < NTB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s & 1][i], fb[s & 1][j],
-                                                              acc[i][j], 0, 0, 0);
-    }
-    // Schedule: the next stage's DMA and this stage's first fragments up front, then each
-    // sub-step's MFMAs with the following sub-step's fragment reads threaded between them.
-    constexpr int NF = VB + NTB;  // fragment reads per sub-step
-    constexpr int NM = VB * NTB;  // MFMAs per sub-step
-    constexpr int NI = NF < NM ? NF : NM;
-    __builtin_amdgcn_sched_group_barrier(0x020, WI + HI, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, NF, 0);
-#pragma unroll
-    for (int s = 0; s < 3; ++s) {
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      if constexpr (NF > NI) __builtin_amdgcn_sched_group_barrier(0x100, NF - NI, 0);
-      if constexpr (NM > NI) __builtin_amdgcn_sched_group_barrier(0x008, NM - NI, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+  // K loop: stages of 64 K, two LDS buffers (distinct objects, so a DMA into one never makes the
+  // compiler wait before reads of the other). Stage k: sub-steps 0-2 run from the fragments in
+  // registers while reading the next sub-step's; then this wave's DMA of stage k+1 is waited
+  // and all waves meet (stage k+1 has landed everywhere, and every read of stage k's buffer is
+  // done); sub-step 3 then issues the DMA of stage k+2 into stage k's buffer and reads the
+  // first fragments of stage k+1. The DMA index is clamped at the last stage and the final
+  // fragment reads are unused: one uniform path, in bounds. H is a multiple of 128, so the
+  // stage count is even and the two buffers alternate statically.
+  const int nk = H / kKStage;
+  auto stage = [&](int k, uint8_t* cw, uint8_t* ch, const uint8_t* nw, const uint8_t* nh) {
+    mfmas(0);
+    load_frags(cw, ch, 1, 1);
+    sched_sub(ICR{}, IC0{});
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(1);
+    load_frags(cw, ch, 2, 0);
+    sched_sub(ICR{}, IC0{});
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(0);
+    load_frags(cw, ch, 3, 1);
+    sched_sub(ICR{}, IC0{});
+    __builtin_amdgcn_sched_barrier(0);
     wait_dma();
     __syncthreads();
+    issue(k + 2 < nk ? k + 2 : nk - 1, cw, ch);
+    mfmas(1);
+    load_frags(nw, nh, 0, 0);
+    sched_sub(ICR{}, ICD{});
+    __builtin_amdgcn_sched_barrier(0);
   };
-
-  const int nk = H / kKStage;
   issue(0, lds_w0, lds_h0);
-  wait_dma();
+  issue(nk > 1 ? 1 : 0, lds_w1, lds_h1);
+  __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(WI + HI) : "memory");
   __syncthreads();
-  int kc = 0;
-  for (; kc + 1 < nk; kc += 2) {
-    stage(kc, nk, lds_w0, lds_h0, lds_w1, lds_h1);
-    stage(kc + 1, nk, lds_w1, lds_h1, lds_w0, lds_h0);
+  load_frags(lds_w0, lds_h0, 0, 0);
+  for (int k = 0; k < nk; k += 2) {
+    stage(k, lds_w0, lds_h0, lds_w1, lds_h1);
+    stage(k + 1, lds_w1, lds_h1, lds_w0, lds_h0);
   }
-  if (kc < nk) stage(kc, nk, lds_w0, lds_h0, lds_w1, lds_h1);
+  wait_dma();
 
   // ---------------------------------- epilogue ----------------------------------
   if constexpr (TEMP) {
@@ -594,7 +627,7 @@ static hipError_t launch_variant(const LmheadArgs& a, bool ent, hipStream_t s) {
 
 hipError_t launch_lmhead(const LmheadArgs& a, int bt, bool ent, hipStream_t s) {
   switch (bt) {
-    case 256: return launch_variant<1, 4, 2>(a, ent, s);
+    case 256: return launch_variant<2, 2, 4>(a, ent, s);
     case 128: return launch_variant<2, 2, 2>(a, ent, s);
     case 64: return launch_variant<4, 1, 2>(a, ent, s);
     case 32: return launch_variant<4, 1, 1>(a, ent, s);

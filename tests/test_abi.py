@@ -74,6 +74,7 @@ def test_layout_check_counts_launches(lib):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(hidden_size=100, vocab_size=1000), _lib.RLK_ERR_UNSUPPORTED_SHAPE),
+    (dict(hidden_size=192, vocab_size=1000), _lib.RLK_ERR_UNSUPPORTED_SHAPE),
     (dict(hidden_size=256, vocab_size=1001), _lib.RLK_ERR_UNSUPPORTED_SHAPE),
     (dict(hidden_size=256, vocab_size=1000, vocab_segments=3), _lib.RLK_ERR_UNSUPPORTED_SHAPE),
     (dict(hidden_size=256, vocab_size=1000, vocab_segments=16), _lib.RLK_ERR_UNSUPPORTED_SHAPE),

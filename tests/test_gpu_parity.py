@@ -58,7 +58,7 @@ SHAPES = [
     (513, 384, 3000, 2, 0.7, True),    # 2 segments of 1500 = 5 tiles + 220, temperature
     (33, 1024, 1000, 1, 1.0, False),   # one segment, 3 full tiles + 232
     (1, 128, 4000, 8, 1.0, True),      # a single row, 8 segments of 500
-    (1030, 64, 768, 4, 1.3, True),     # many row tiles, 3 partial tiles of 192
+    (1030, 128, 768, 4, 1.3, True),    # many row tiles, 3 partial tiles of 192
 ]
 
 
@@ -92,7 +92,7 @@ def test_exact_gemm_case_is_tight(rlk):
 
 @pytest.mark.parametrize("V", [1000, 151936])
 def test_uniform_logits_give_minus_log_V(rlk, V):
-    T, H = 40, 64
+    T, H = 40, 128
     h = np.zeros((T, H), np.uint16)
     W = datagen.normal_bf16(V, H, 120, 1, scale=0.02)
     y = np.random.default_rng(1).integers(0, V, size=T).astype(np.int32)
