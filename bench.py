@@ -142,6 +142,91 @@ def cpu_baseline(h, Wb, y, budget_s: float = 10.0, max_reps: int = 8) -> dict:
             "_rows": rows, "_logp": res["logp"]}
 
 
+def time_layout(rlk, lp, hd, Wd, yd, gd, T, steps, warmup, layout_kw, flops_per_launch=None):
+    """Time full forwards in one layout: step time, and the LM-head launches' summed duration
+    from HIP events the library records around each launch. Returns host logp too."""
+    import numpy as np
+    import torch
+
+    dev = hd.device
+    layout, keep = rlk.make_layout(T, **layout_kw)
+    n_launch = rlk.rlk_layout_check(lp.config, layout)
+    ws_bytes = rlk.rlk_logprob_workspace_size(lp.config, layout)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    logp = torch.empty(T, dtype=torch.float32, device=dev)
+    lse = torch.empty(T, dtype=torch.float32, device=dev)
+    ent = torch.empty(T, dtype=torch.float32, device=dev) if lp.entropy else None
+    sp = torch.cuda.current_stream(dev).cuda_stream
+
+    def ptr(t):
+        return None if t is None else t.data_ptr()
+
+    def step(events=()):
+        rlk.rlk_logprob_forward_timed(lp.handle, hd.data_ptr(), Wd.data_ptr(), yd.data_ptr(),
+                                      layout, ptr(gd), logp.data_ptr(), lse.data_ptr(), ptr(ent),
+                                      ws.data_ptr(), ws_bytes, sp, list(events))
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = HipEvents(2 + 2 * n_launch * steps)
+    ev.record(0, sp)
+    for i in range(steps):
+        base = 2 + 2 * n_launch * i
+        step(ev.ev[base:base + 2 * n_launch])
+    ev.record(1, sp)
+    torch.cuda.synchronize()
+    total = ev.ms(0, 1)
+    kern = sum(ev.ms(2 + 2 * j, 3 + 2 * j) for j in range(n_launch * steps))
+    ev.close()
+    del keep
+    return {"ms_per_step": total / steps, "lmhead_ms_per_step": kern / steps,
+            "lmhead_launches_per_step": n_launch, "_logp": logp.cpu().numpy().copy()}
+
+
+def extras(rlk, datagen, np, torch, hd, Wd, yd, w, ref_logp) -> dict:
+    """The other rows of the path, measured next to the headline: the rollout layout of the TP4
+    workload (decode batches x 4 vocab shards; HBM-bound W stream) and the fused final RMSNorm +
+    temperature + entropy head."""
+    out = {}
+    lp = rlk.Logprob(w.H, w.V, vocab_segments=w.segments, device=0)
+    sizes = datagen.decode_layout(w.T)
+    r = time_layout(rlk, lp, hd, Wd, yd, None, w.T, 3, 1,
+                    dict(batch_sizes=sizes, vocab_shards=4))
+    w_bytes = r["lmhead_launches_per_step"] * (w.V // 4) * w.H * 2
+    out["tp4_decode_x4_shards"] = {
+        "decode_batches": len(sizes), "lmhead_launches_per_step": r["lmhead_launches_per_step"],
+        "ms_per_step": r["ms_per_step"], "tokens_per_s": w.T / (r["ms_per_step"] * 1e-3),
+        "w_stream_GBps": w_bytes / (r["lmhead_ms_per_step"] * 1e-3) / 1e9,
+        "hbm_frac": w_bytes / (r["lmhead_ms_per_step"] * 1e-3) / 8e12,
+        "mismatch_count_vs_one_pass": int(np.count_nonzero(
+            r["_logp"].view(np.uint32) != ref_logp.view(np.uint32)))}
+    del lp
+    wn = datagen.WORKLOADS["norm_head"]
+    log("norm_head inputs")
+    x = datagen.hidden_bits(wn)
+    Wn = datagen.weight_bits(wn)
+    g = datagen.gamma_bits(wn)
+    yn = np.load(os.path.join(ROOT, "tests", "golden", "targets_norm_head.npy"))
+    dev = hd.device
+    xd = torch.from_numpy(x.view(np.int16)).to(dev)
+    Wnd = torch.from_numpy(Wn.view(np.int16)).to(dev)
+    gd = torch.from_numpy(g.view(np.int16)).to(dev)
+    ynd = torch.from_numpy(yn.astype(np.int32)).to(dev)
+    del x, Wn
+    lpn = rlk.Logprob(wn.H, wn.V, vocab_segments=wn.segments, temperature=wn.tau, rmsnorm=True,
+                      rms_eps=wn.rms_eps, entropy=True, device=0)
+    r = time_layout(rlk, lpn, xd, Wnd, ynd, gd, wn.T, 5, 2, {})
+    fl = 2.0 * wn.T * wn.H * wn.V
+    out["norm_head_one_pass"] = {
+        "T": wn.T, "H": wn.H, "V": wn.V, "tau": wn.tau, "ms_per_step": r["ms_per_step"],
+        "tokens_per_s": wn.T / (r["ms_per_step"] * 1e-3),
+        "lmhead_ms": r["lmhead_ms_per_step"],
+        "lmhead_frac_of_bf16_peak": fl / (r["lmhead_ms_per_step"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    del xd, Wnd, lpn
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -151,6 +236,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-layout-check", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0)
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the rollout-layout and norm_head measurements")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -259,6 +346,9 @@ def main() -> int:
         "layout_mismatch_count": mismatch,
         "traffic_note": traffic_note,
     }
+    if not args.no_extras:
+        log("extras: rollout layout (decode batches x 4 shards), norm_head")
+        result["extras"] = extras(rlk, datagen, np, torch, hd, Wd, yd, w, out_logp)
     if not args.no_cpu_baseline:
         log("cpu baseline (float64 oracle on a bounded sample)")
         cb = cpu_baseline(h, Wb, y)
