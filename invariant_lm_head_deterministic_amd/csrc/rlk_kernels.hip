@@ -112,6 +112,185 @@ __device__ __forceinline__ float tree_sum(const float* v) {
   }
 }
 
+// Where a block's work lies: vocab tile (segment, index in segment, global index, columns) and
+// row tile (first row, rows present).
+struct Tile {
+  int64_t start;  // global vocab index of the tile's first column
+  int len;        // columns in the tile (256, or fewer for a segment's last tile)
+  int g;          // global tile index
+  int row0;       // first launch row of the row tile
+  int rows;       // rows present in the row tile
+};
+
+// Block -> (vocab tile, row tile), XCD-aware: consecutive block ids go round-robin to the 8 XCDs,
+// so remap them so that each XCD walks a contiguous range of vocab tiles, a group of 8 vocab
+// tiles at a time across all row tiles (W tiles and hidden tiles shared in L2; 8 was the best of
+// 2, 4, 8, 16 measured on the Qwen3-8B head). Returns false for the few padding blocks.
+template <int BT>
+__device__ __forceinline__ bool map_tile(const LmheadArgs& a, Tile& t) {
+  const int n_vt = a.n_seg * a.tiles_per_seg;
+  const int n_tt = (a.rows + BT - 1) / BT;
+  const int64_t n_items = (int64_t)n_vt * n_tt;
+  const int64_t per_xcd = (int64_t)gridDim.x / 8;
+  const int64_t L = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (L >= n_items) return false;
+  constexpr int GV = 8;
+  const int64_t grp = L / ((int64_t)GV * n_tt);
+  const int first_v = (int)(grp * GV);
+  const int gsz = min(GV, n_vt - first_v);
+  const int64_t within = L - grp * GV * n_tt;
+  const int vt = first_v + (int)(within % gsz);
+  const int tt = (int)(within / gsz);
+  const int seg = a.seg_begin + vt / a.tiles_per_seg;
+  const int jt = vt % a.tiles_per_seg;
+  t.start = (int64_t)seg * a.seg_len + (int64_t)jt * kVocabTile;
+  t.len = (int)min((int64_t)kVocabTile, a.seg_len - (int64_t)jt * kVocabTile);
+  t.g = seg * a.tiles_per_seg + jt;
+  t.row0 = tt * BT;
+  t.rows = min(BT, a.rows - t.row0);
+  return true;
+}
+
+// Fused tile epilogue (C2, C4-C7) on the MFMA result registers of one wave. The wave owns
+// VB = 8 / VW of the tile's 32-column blocks (wave index wv) and NTB row blocks of 32 (row block
+// wt * NTB + j). For VW > 1 the tile max and the upper levels of the sum tree cross waves through
+// LDS (red_m [VW][BT], red_s and red_u [VW][2][BT]); every wave of the block must call this.
+template <int VW, int TW, int NTB, bool ENT, bool TEMP>
+__device__ __forceinline__ void tile_epilogue(f32x16 (&acc)[8 / VW][NTB], const LmheadArgs& a,
+                                              const Tile& t, int wv, int wt, int half, int col,
+                                              float* red_m, float* red_s, float* red_u) {
+  constexpr int VB = 8 / VW;
+  constexpr int BT = 32 * NTB * TW;
+  if constexpr (TEMP) {
+#pragma unroll
+    for (int i = 0; i < VB; ++i)
+#pragma unroll
+      for (int j = 0; j < NTB; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = acc[i][j][r] * a.inv_tau;
+  }
+  const bool partial = t.len < kVocabTile;
+  const int tile_len = t.len;
+  // column offset inside the tile of (block i, register r) for this lane
+  auto coff = [&](int i, int r) { return 32 * (wv * VB + i) + 8 * (r >> 2) + 4 * half + (r & 3); };
+
+  float m[NTB];
+#pragma unroll
+  for (int j = 0; j < NTB; ++j) {
+    float mm = -INFINITY;
+    if (partial) {
+#pragma unroll
+      for (int i = 0; i < VB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (coff(i, r) < tile_len) mm = fmaxf(mm, acc[i][j][r]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < VB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mm = fmaxf(mm, acc[i][j][r]);
+    }
+    m[j] = fmaxf(mm, __shfl_xor(mm, 32));
+  }
+  if constexpr (VW > 1) {
+#pragma unroll
+    for (int j = 0; j < NTB; ++j)
+      if (half == 0) red_m[wv * BT + 32 * (wt * NTB + j) + col] = m[j];
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NTB; ++j) {
+      float mm = red_m[32 * (wt * NTB + j) + col];
+#pragma unroll
+      for (int w = 1; w < VW; ++w) mm = fmaxf(mm, red_m[w * BT + 32 * (wt * NTB + j) + col]);
+      m[j] = mm;
+    }
+  }
+
+  float qs[NTB], qu[NTB];
+#pragma unroll
+  for (int j = 0; j < NTB; ++j) {
+    float p[VB], pu[VB];
+#pragma unroll
+    for (int i = 0; i < VB; ++i) {
+      float ps = 0.0f, pq = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float d = acc[i][j][r] - m[j];
+        float e = c_exp(d);
+        if (partial && coff(i, r) >= tile_len) e = 0.0f;
+        ps = ps + e;
+        if constexpr (ENT) {
+          float q = e * d;
+          if (partial && coff(i, r) >= tile_len) q = 0.0f;
+          pq = pq + q;
+        }
+      }
+      p[i] = ps;
+      pu[i] = pq;
+    }
+    qs[j] = tree_sum<VB>(p);
+    if constexpr (ENT) qu[j] = tree_sum<VB>(pu);
+  }
+
+  if constexpr (VW > 1) {
+#pragma unroll
+    for (int j = 0; j < NTB; ++j) {
+      red_s[(wv * 2 + half) * BT + 32 * (wt * NTB + j) + col] = qs[j];
+      if constexpr (ENT) red_u[(wv * 2 + half) * BT + 32 * (wt * NTB + j) + col] = qu[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NTB; ++j) {
+      float v[VW], vu[VW];
+#pragma unroll
+      for (int w = 0; w < VW; ++w) {
+        v[w] = red_s[(w * 2 + half) * BT + 32 * (wt * NTB + j) + col];
+        if constexpr (ENT) vu[w] = red_u[(w * 2 + half) * BT + 32 * (wt * NTB + j) + col];
+      }
+      qs[j] = tree_sum<VW>(v);
+      if constexpr (ENT) qu[j] = tree_sum<VW>(vu);
+    }
+  }
+
+  // halves: s = P[0] + P[1] (fp32 addition is commutative, so both lanes agree)
+  float* __restrict__ pm = a.part_m + (int64_t)(t.g - a.g_base) * a.ld;
+  float* __restrict__ psum = a.part_s + (int64_t)(t.g - a.g_base) * a.ld;
+#pragma unroll
+  for (int j = 0; j < NTB; ++j) {
+    const float sum = qs[j] + __shfl_xor(qs[j], 32);
+    float u = 0.0f;
+    if constexpr (ENT) u = qu[j] + __shfl_xor(qu[j], 32);
+    const int rr = 32 * (wt * NTB + j) + col;  // row inside the row tile
+    if (wv == 0 && half == 0 && rr < t.rows) {
+      const int64_t row = (int64_t)t.row0 + rr;
+      pm[row] = m[j];
+      psum[row] = sum;
+      if constexpr (ENT) a.part_u[(int64_t)(t.g - a.g_base) * a.ld + row] = u;
+    }
+  }
+
+  // target ownership: the lane whose registers hold column y_t of this tile writes z'[t, y_t]
+#pragma unroll
+  for (int j = 0; j < NTB; ++j) {
+    const int rr = 32 * (wt * NTB + j) + col;
+    int y = -1;
+    if (rr < t.rows) y = a.targets[t.row0 + rr];
+    const int64_t d = (int64_t)y - t.start;
+    const bool in_tile = y >= 0 && d >= 0 && d < tile_len;
+    const int dd = (int)d;
+    const bool mine = in_tile && ((dd >> 5) / VB == wv) && (((dd >> 2) & 1) == half);
+    if (__any(mine)) {
+      const int ridx = ((dd >> 5) % VB) * 16 + ((dd >> 3) & 3) * 4 + (dd & 3);
+      float v = 0.0f;
+#pragma unroll
+      for (int i = 0; i < VB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v = (i * 16 + r == ridx) ? acc[i][j][r] : v;
+      if (mine) a.tgt[t.row0 + rr] = v;
+    }
+  }
+}
+
 // --------------------------------------------------------------------------------------------
 // K1: LM-head tile kernel. One block = one vocab tile (256 columns of one segment) x BT rows.
 // Waves: VW split the tile's 8 column blocks, TW split the rows; each wave owns VB = 8/VW column
@@ -137,39 +316,20 @@ k_lmhead(const LmheadArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds_w1[kVocabTile * kRowBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_h0[BT * kRowBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_h1[BT * kRowBytes];
-  __shared__ float red_m[VW > 1 ? VW : 1][BT];
-  __shared__ float red_s[VW > 1 ? VW : 1][2][BT];
-  __shared__ float red_u[(VW > 1 && ENT) ? VW : 1][2][BT];
+  __shared__ float red_m[(VW > 1 ? VW : 1) * BT];
+  __shared__ float red_s[(VW > 1 ? VW : 1) * 2 * BT];
+  __shared__ float red_u[(VW > 1 && ENT ? VW : 1) * 2 * BT];
 
-  // ---- block -> (vocab tile, row tile), XCD-aware: consecutive block ids go round-robin to
-  // the 8 XCDs, so remap them so that each XCD walks a contiguous range of vocab tiles, a group
-  // of 8 vocab tiles at a time across all row tiles (W tiles and hidden tiles shared in L2; 8 was
-  // the best of 2, 4, 8, 16 measured on the Qwen3-8B head).
-  const int n_vt = a.n_seg * a.tiles_per_seg;
-  const int n_tt = (a.rows + BT - 1) / BT;
-  const int64_t n_items = (int64_t)n_vt * n_tt;
-  const int64_t per_xcd = (int64_t)gridDim.x / 8;
-  const int64_t L = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  if (L >= n_items) return;
-  constexpr int GV = 8;
-  const int64_t grp = L / ((int64_t)GV * n_tt);
-  const int first_v = (int)(grp * GV);
-  const int gsz = min(GV, n_vt - first_v);
-  const int64_t within = L - grp * GV * n_tt;
-  const int vt = first_v + (int)(within % gsz);
-  const int tt = (int)(within / gsz);
-
-  const int seg = a.seg_begin + vt / a.tiles_per_seg;
-  const int jt = vt % a.tiles_per_seg;
-  const int64_t tile_start = (int64_t)seg * a.seg_len + (int64_t)jt * kVocabTile;
-  const int tile_len = (int)min((int64_t)kVocabTile, a.seg_len - (int64_t)jt * kVocabTile);
-  const int gtile = seg * a.tiles_per_seg + jt;
-  const int row0 = tt * BT;
+  Tile t;
+  if (!map_tile<BT>(a, t)) return;
+  const int64_t tile_start = t.start;
+  const int tile_len = t.len;
+  const int row0 = t.row0;
   const int H = a.H;
 
   const uint16_t* __restrict__ Wt = a.W + (tile_start - a.w_row0) * (int64_t)H;
   const uint16_t* __restrict__ Ht = a.hidden + (int64_t)row0 * H;
-  const int rows_here = min(BT, a.rows - row0);
+  const int rows_here = t.rows;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -309,134 +469,175 @@ k_lmhead(const LmheadArgs a) {
   stage(std::false_type{}, k, lds_w0, lds_h0, lds_w1, lds_h1);
   stage(std::false_type{}, k + 1, lds_w1, lds_h1, lds_w0, lds_h0);
 
-  // ---------------------------------- epilogue ----------------------------------
-  if constexpr (TEMP) {
+  tile_epilogue<VW, TW, NTB, ENT, TEMP>(acc, a, t, wv, wt, half, col, red_m, red_s, red_u);
+}
+
+// --------------------------------------------------------------------------------------------
+// K1d: deep-pipeline LM-head tile kernel for launches of few rows (decode batches). Same tiles,
+// same MFMA chain (C1), same fragment order and the same epilogue as k_lmhead, hence the same
+// bits; only the staging depth differs. A decode batch has one or two row tiles, so a launch
+// has few blocks and the W stream is bound by the bytes each block keeps in flight: these
+// variants cycle NS (3-4) LDS stages, so NS-1 stages of DMA are outstanding while one is read.
+// The stage buffer is picked at run time; the DMA is issued from inline assembly so that the
+// compiler, which cannot tell the stage buffers apart at run time, does not wait for every
+// outstanding DMA before each LDS read. Its completion is awaited explicitly (vmcnt) before the
+// barrier that publishes a stage, exactly as in k_lmhead.
+// --------------------------------------------------------------------------------------------
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor (base, unstrided, `bytes` long, 32-bit data format) in 4 SGPRs.
+__device__ __forceinline__ i32x4 buffer_desc(const void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)base;
+  i32x4 d;
+  d[0] = (int32_t)(uint32_t)b;
+  d[1] = (int32_t)((uint32_t)(b >> 32) & 0xffffu);
+  d[2] = (int32_t)bytes;
+  d[3] = 0x00020000;
+  return d;
+}
+
+// buffer_load_dwordx4 ... lds: lane l's 16 bytes at voff + soff land at LDS byte lds_addr + 16 l.
+__device__ __forceinline__ void dma16_asm(i32x4 desc, uint32_t lds_addr, uint32_t voff,
+                                          uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(desc), "s"(soff)
+               : "memory");
+}
+
+template <int D>
+__device__ __forceinline__ void wait_vm() {
+  __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(D) : "memory");
+}
+
+template <int VW, int TW, int NTB, int NS, bool ENT, bool TEMP>
+__global__ void __launch_bounds__(64 * VW * TW) k_lmhead_deep(const LmheadArgs a) {
+  constexpr int NWAVES = VW * TW;
+  constexpr int BT = 32 * NTB * TW;
+  constexpr int VB = 8 / VW;
+  constexpr int WI = kVocabTile / 8 / NWAVES;
+  constexpr int HI = BT / 8 / NWAVES;
+  constexpr int DPS = WI + HI;  // DMA instructions per wave per stage
+  constexpr int SW = kVocabTile * kRowBytes;
+  constexpr int SH = BT * kRowBytes;
+  static_assert(VB * VW == 8 && WI * 8 * NWAVES == kVocabTile && HI * 8 * NWAVES == BT, "tiling");
+  static_assert(NS >= 2 && NS <= 4 && (NS - 2) * DPS <= 63, "stages");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_w[NS * SW];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_h[NS * SH];
+  __shared__ float red_m[(VW > 1 ? VW : 1) * BT];
+  __shared__ float red_s[(VW > 1 ? VW : 1) * 2 * BT];
+  __shared__ float red_u[(VW > 1 && ENT ? VW : 1) * 2 * BT];
+
+  Tile t;
+  if (!map_tile<BT>(a, t)) return;
+  const int H = a.H;
+  const uint16_t* __restrict__ Wt = a.W + (t.start - a.w_row0) * (int64_t)H;
+  const uint16_t* __restrict__ Ht = a.hidden + (int64_t)t.row0 * H;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wv = wave % VW;
+  const int wt = wave / VW;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+
+  uint32_t wgo[WI], hgo[HI];
+#pragma unroll
+  for (int q = 0; q < WI; ++q) {
+    const int r = 8 * (q * NWAVES + wave) + (lane >> 3);
+    const int c = (lane & 7) ^ swz(r);
+    wgo[q] = (uint32_t)(min(r, t.len - 1) * H + c * 8) * 2u;
+  }
+#pragma unroll
+  for (int q = 0; q < HI; ++q) {
+    const int r = 8 * (q * NWAVES + wave) + (lane >> 3);
+    const int c = (lane & 7) ^ swz(r);
+    hgo[q] = (uint32_t)(min(r, t.rows - 1) * H + c * 8) * 2u;
+  }
+  const i32x4 dw = buffer_desc(Wt, (uint32_t)(t.len * H * 2));
+  const i32x4 dh = buffer_desc(Ht, (uint32_t)(t.rows * H * 2));
+  const uint32_t lw0 = (uint32_t)(uintptr_t)lds_w + 8 * wave * kRowBytes;
+  const uint32_t lh0 = (uint32_t)(uintptr_t)lds_h + 8 * wave * kRowBytes;
+  const int nk = H / kKStage;
+  auto issue = [&](int kc) {
+    const int b = kc % NS;
+    const uint32_t so = (uint32_t)kc * kRowBytes;
+#pragma unroll
+    for (int q = 0; q < WI; ++q)
+      dma16_asm(dw, lw0 + b * SW + 8 * q * NWAVES * kRowBytes, wgo[q], so);
+#pragma unroll
+    for (int q = 0; q < HI; ++q)
+      dma16_asm(dh, lh0 + b * SH + 8 * q * NWAVES * kRowBytes, hgo[q], so);
+  };
+
+  f32x16 acc[VB][NTB];
+#pragma unroll
+  for (int i = 0; i < VB; ++i)
+#pragma unroll
+    for (int j = 0; j < NTB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int sw = swz(col);
+  int loff[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) loff[s] = col * kRowBytes + (((2 * s + half) ^ sw) << 4);
+  const int a0 = 32 * wv * VB * kRowBytes, b0 = 32 * wt * NTB * kRowBytes;
+  bf16x8 fa[2][VB], fb[2][NTB];
+  auto load_frags = [&](int buf, int s, int slot) {
+    const uint8_t* pa = lds_w + buf * SW + a0 + loff[s];
+    const uint8_t* pb = lds_h + buf * SH + b0 + loff[s];
+#pragma unroll
+    for (int i = 0; i < VB; ++i) fa[slot][i] = *(const bf16x8*)(pa + i * 32 * kRowBytes);
+#pragma unroll
+    for (int j = 0; j < NTB; ++j) fb[slot][j] = *(const bf16x8*)(pb + j * 32 * kRowBytes);
+  };
+  auto mfmas = [&](int slot) {
 #pragma unroll
     for (int i = 0; i < VB; ++i)
 #pragma unroll
       for (int j = 0; j < NTB; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = acc[i][j][r] * a.inv_tau;
-  }
-  const bool partial = tile_len < kVocabTile;
-  // column offset inside the tile of (block i, register r) for this lane
-  auto coff = [&](int i, int r) { return 32 * (wv * VB + i) + 8 * (r >> 2) + 4 * half + (r & 3); };
-
-  float m[NTB];
-#pragma unroll
-  for (int j = 0; j < NTB; ++j) {
-    float mm = -INFINITY;
-    if (partial) {
-#pragma unroll
-      for (int i = 0; i < VB; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (coff(i, r) < tile_len) mm = fmaxf(mm, acc[i][j][r]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < VB; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mm = fmaxf(mm, acc[i][j][r]);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j],
+                                                            0, 0, 0);
+  };
+  // wait until the DMA of stage k+1 is done while up to `later` younger stages stay in flight
+  auto wait_stage = [&](int later) {
+    if constexpr (NS >= 4) {
+      if (later >= 2) { wait_vm<2 * DPS>(); return; }
     }
-    m[j] = fmaxf(mm, __shfl_xor(mm, 32));
-  }
-  if constexpr (VW > 1) {
-#pragma unroll
-    for (int j = 0; j < NTB; ++j)
-      if (half == 0) red_m[wv][32 * (wt * NTB + j) + col] = m[j];
+    if constexpr (NS >= 3) {
+      if (later >= 1) { wait_vm<DPS>(); return; }
+    }
+    wait_vm<0>();
+  };
+
+  // prologue: stages 0 .. NS-1 in flight, wait for stage 0
+  const int pro = nk < NS ? nk : NS;
+  for (int j = 0; j < pro; ++j) issue(j);
+  wait_stage(pro - 1 > NS - 2 ? NS - 2 : pro - 1);
+  // (the youngest pro-1 stages may still be in flight; stage 0 has landed for this wave)
+  __syncthreads();
+  load_frags(0, 0, 0);
+  for (int k = 0; k < nk; ++k) {
+    const int b = k % NS;
+    mfmas(0);
+    load_frags(b, 1, 1);
+    mfmas(1);
+    load_frags(b, 2, 0);
+    mfmas(0);
+    load_frags(b, 3, 1);
+    // stage k+1 must have landed for every wave; stages k+2 .. k+NS-1 may stay in flight
+    const int issued_last = (k - 1 + NS < nk - 1 ? k - 1 + NS : nk - 1);  // newest stage issued
+    wait_stage(issued_last - (k + 1));
     __syncthreads();
-#pragma unroll
-    for (int j = 0; j < NTB; ++j) {
-      float mm = red_m[0][32 * (wt * NTB + j) + col];
-#pragma unroll
-      for (int w = 1; w < VW; ++w) mm = fmaxf(mm, red_m[w][32 * (wt * NTB + j) + col]);
-      m[j] = mm;
-    }
+    if (k + NS < nk) issue(k + NS);  // into stage k's buffer, free after the barrier
+    mfmas(1);
+    load_frags((k + 1) % NS, 0, 0);
   }
+  wait_vm<0>();
 
-  float qs[NTB], qu[NTB];
-#pragma unroll
-  for (int j = 0; j < NTB; ++j) {
-    float p[VB], pu[VB];
-#pragma unroll
-    for (int i = 0; i < VB; ++i) {
-      float ps = 0.0f, pq = 0.0f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float d = acc[i][j][r] - m[j];
-        float e = c_exp(d);
-        if (partial && coff(i, r) >= tile_len) e = 0.0f;
-        ps = ps + e;
-        if constexpr (ENT) {
-          float t = e * d;
-          if (partial && coff(i, r) >= tile_len) t = 0.0f;
-          pq = pq + t;
-        }
-      }
-      p[i] = ps;
-      pu[i] = pq;
-    }
-    qs[j] = tree_sum<VB>(p);
-    if constexpr (ENT) qu[j] = tree_sum<VB>(pu);
-  }
-
-  if constexpr (VW > 1) {
-#pragma unroll
-    for (int j = 0; j < NTB; ++j) {
-      red_s[wv][half][32 * (wt * NTB + j) + col] = qs[j];
-      if constexpr (ENT) red_u[wv][half][32 * (wt * NTB + j) + col] = qu[j];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < NTB; ++j) {
-      float v[VW], vu[VW];
-#pragma unroll
-      for (int w = 0; w < VW; ++w) {
-        v[w] = red_s[w][half][32 * (wt * NTB + j) + col];
-        if constexpr (ENT) vu[w] = red_u[w][half][32 * (wt * NTB + j) + col];
-      }
-      qs[j] = tree_sum<VW>(v);
-      if constexpr (ENT) qu[j] = tree_sum<VW>(vu);
-    }
-  }
-
-  // halves: s = P[0] + P[1] (fp32 addition is commutative, so both lanes agree)
-  float* __restrict__ pm = a.part_m + (int64_t)(gtile - a.g_base) * a.ld;
-  float* __restrict__ psum = a.part_s + (int64_t)(gtile - a.g_base) * a.ld;
-#pragma unroll
-  for (int j = 0; j < NTB; ++j) {
-    const float s = qs[j] + __shfl_xor(qs[j], 32);
-    float u = 0.0f;
-    if constexpr (ENT) u = qu[j] + __shfl_xor(qu[j], 32);
-    const int rr = 32 * (wt * NTB + j) + col;  // row inside the row tile
-    if (wv == 0 && half == 0 && rr < rows_here) {
-      const int64_t t = (int64_t)row0 + rr;
-      pm[t] = m[j];
-      psum[t] = s;
-      if constexpr (ENT) a.part_u[(int64_t)(gtile - a.g_base) * a.ld + t] = u;
-    }
-  }
-
-  // target ownership: the lane whose registers hold column y_t of this tile writes z'[t, y_t]
-#pragma unroll
-  for (int j = 0; j < NTB; ++j) {
-    const int rr = 32 * (wt * NTB + j) + col;
-    int y = -1;
-    if (rr < rows_here) y = a.targets[row0 + rr];
-    const int64_t d = (int64_t)y - tile_start;
-    const bool in_tile = y >= 0 && d >= 0 && d < tile_len;
-    const int dd = (int)d;
-    const bool mine = in_tile && ((dd >> 5) / VB == wv) && (((dd >> 2) & 1) == half);
-    if (__any(mine)) {
-      const int ridx = ((dd >> 5) % VB) * 16 + ((dd >> 3) & 3) * 4 + (dd & 3);
-      float v = 0.0f;
-#pragma unroll
-      for (int i = 0; i < VB; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) v = (i * 16 + r == ridx) ? acc[i][j][r] : v;
-      if (mine) a.tgt[row0 + rr] = v;
-    }
-  }
+  tile_epilogue<VW, TW, NTB, ENT, TEMP>(acc, a, t, wv, wt, half, col, red_m, red_s, red_u);
 }
 
 // --------------------------------------------------------------------------------------------
@@ -632,12 +833,33 @@ static hipError_t launch_variant(const LmheadArgs& a, bool ent, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int VW, int TW, int NTB, int NS>
+static hipError_t launch_deep(const LmheadArgs& a, bool ent, hipStream_t s) {
+  constexpr int BT = 32 * NTB * TW;
+  const int64_t n_vt = (int64_t)a.n_seg * a.tiles_per_seg;
+  const int64_t n_tt = (a.rows + BT - 1) / BT;
+  const int64_t items = n_vt * n_tt;
+  const int64_t blocks = (items + 7) / 8 * 8;
+  if (items == 0) return hipSuccess;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)blocks), block(64 * VW * TW);
+  const bool temp = a.inv_tau != 1.0f;
+  if (ent) {
+    if (temp) hipLaunchKernelGGL((k_lmhead_deep<VW, TW, NTB, NS, true, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_lmhead_deep<VW, TW, NTB, NS, true, false>), grid, block, 0, s, a);
+  } else {
+    if (temp) hipLaunchKernelGGL((k_lmhead_deep<VW, TW, NTB, NS, false, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_lmhead_deep<VW, TW, NTB, NS, false, false>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_lmhead(const LmheadArgs& a, int bt, bool ent, hipStream_t s) {
   switch (bt) {
     case 256: return launch_variant<2, 2, 4>(a, ent, s);
-    case 128: return launch_variant<2, 2, 2>(a, ent, s);
-    case 64: return launch_variant<4, 1, 2>(a, ent, s);
-    case 32: return launch_variant<4, 1, 1>(a, ent, s);
+    case 128: return launch_deep<2, 2, 2, 3>(a, ent, s);
+    case 64: return launch_deep<4, 1, 2, 3>(a, ent, s);
+    case 32: return launch_deep<4, 1, 1, 4>(a, ent, s);
     default: return hipErrorInvalidValue;
   }
 }
