@@ -856,7 +856,7 @@ static hipError_t launch_deep(const LmheadArgs& a, bool ent, hipStream_t s) {
 
 hipError_t launch_lmhead(const LmheadArgs& a, int bt, bool ent, hipStream_t s) {
   switch (bt) {
-    case 256: return launch_variant<2, 2, 4>(a, ent, s);
+    case 256: return launch_variant<2, 4, 2>(a, ent, s);
     case 128: return launch_deep<2, 2, 2, 3>(a, ent, s);
     case 64: return launch_deep<4, 1, 2, 3>(a, ent, s);
     case 32: return launch_deep<4, 1, 1, 4>(a, ent, s);
