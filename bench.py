@@ -13,6 +13,19 @@ oracle timed on a bounded sample of the same rows.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
     python bench.py --copy-calibration-mib 1024   # a plain device copy, for PMC byte scaling
+    python bench.py --pmc-summary DIR             # profiles/ summaries from rocprofv3 output
+
+The PMC summary (profiles/lmhead_qwen3_8b_head_pmc.txt) is written from five rocprofv3 runs of
+this script, each into its own folder under DIR (the commands are printed into the summary):
+  stats   --kernel-trace --stats, default step counts     (kernel durations)
+  fetch   --pmc FETCH_SIZE GRBM_GUI_ACTIVE --kernel-trace (bytes read from HBM/MALL, clock)
+  write   --pmc WRITE_SIZE SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE --kernel-trace
+  cfetch  --pmc FETCH_SIZE  on --copy-calibration-mib 1024
+  cwrite  --pmc WRITE_SIZE  on --copy-calibration-mib 1024
+FETCH_SIZE and WRITE_SIZE are scaled by what they read for the plain 1 GiB copy. The shader
+clock is GRBM_GUI_ACTIVE (summed over the 8 XCDs, so divided by 8) over the dispatch's duration
+from the kernel trace of the same run; MFMA busy is SQ_VALU_MFMA_BUSY_CYCLES over those cycles
+times the 1024 SIMDs.
 """
 
 from __future__ import annotations
@@ -31,6 +44,10 @@ sys.path.insert(0, ROOT)
 METRIC = "selected-token logprobs/sec at H=4096,V=151936; MFMA util; layout mismatch=0"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "lmhead_qwen3_8b_head_pmc.txt")
+PROFILE_STATS = os.path.join(ROOT, "profiles", "lmhead_qwen3_8b_head_kernel_stats.txt")
+NOMINAL_SCLK_MHZ = 2400.0  # the clock the published MFMA peak is quoted at
+PROF_ARGS = "--steps 3 --warmup 1 --no-cpu-baseline --no-layout-check --no-extras"
+STATS_ARGS = "--steps 30 --warmup 3 --no-cpu-baseline --no-layout-check --no-extras"
 KERNEL_SRC = os.path.join(ROOT, "invariant_lm_head_deterministic_amd", "csrc", "rlk_kernels.hip")
 
 
@@ -74,22 +91,129 @@ def kernel_source_sha() -> str:
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
 
 
-def committed_traffic() -> tuple[float | None, str]:
-    """HBM bytes per LM-head launch from the committed rocprofv3 PMC summary, or None when the
-    summary is missing or was taken on a different kernel source."""
+def committed_pmc() -> tuple[dict, str]:
+    """Per-launch figures of the LM-head kernel from the committed rocprofv3 PMC summary: HBM
+    traffic in bytes, shader clock in MHz, MFMA busy fraction. Empty when the summary is missing
+    or was taken on a different kernel source."""
     if not os.path.exists(PROFILE_TRAFFIC):
-        return None, "no PMC summary committed"
+        return {}, "no PMC summary committed"
     kv = {}
     for line in open(PROFILE_TRAFFIC):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
     if kv.get("kernel_source_sha256") != kernel_source_sha():
-        return None, "kernel changed since the PMC counters were taken"
+        return {}, "kernel changed since the PMC counters were taken"
     try:
-        return float(kv["traffic_bytes_per_launch"]), "rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-scaled"
+        return {"traffic": float(kv["traffic_bytes_per_launch"]),
+                "sclk_mhz": float(kv["sclk_mhz"]),
+                "mfma_busy": float(kv["mfma_busy_frac"])}, \
+            "rocprofv3 FETCH_SIZE+WRITE_SIZE (copy-scaled), GRBM_GUI_ACTIVE, SQ_VALU_MFMA_BUSY_CYCLES"
     except (KeyError, ValueError):
-        return None, "PMC summary incomplete"
+        return {}, "PMC summary incomplete"
+
+
+def _csv(path: str) -> list[dict]:
+    import csv
+
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _one(d: str, suffix: str) -> str:
+    import glob
+
+    hits = sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
+    if not hits:
+        raise FileNotFoundError(f"no *{suffix} under {d}")
+    return hits[0]
+
+
+def _counters(d: str, kernel_sub: str) -> dict[str, list[tuple[int, float]]]:
+    """counter name -> [(dispatch id, value)] for dispatches whose name contains kernel_sub."""
+    out: dict[str, list[tuple[int, float]]] = {}
+    for r in _csv(_one(d, "counter_collection.csv")):
+        if kernel_sub in r["Kernel_Name"]:
+            out.setdefault(r["Counter_Name"], []).append((int(r["Dispatch_Id"]),
+                                                          float(r["Counter_Value"])))
+    return out
+
+
+def _durations(d: str, kernel_sub: str) -> dict[int, int]:
+    return {int(r["Dispatch_Id"]): int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            for r in _csv(_one(d, "kernel_trace.csv")) if kernel_sub in r["Kernel_Name"]}
+
+
+def write_pmc_summary(base: str) -> None:
+    """Write the two profiles/ summaries from the five rocprofv3 runs under ``base``."""
+    cmd = "rocprofv3 {opts} --output-format csv -d {d} -o run -- python -u bench.py {args}"
+    runs = {
+        "stats": ("--kernel-trace --stats", STATS_ARGS),
+        "fetch": ("--pmc FETCH_SIZE GRBM_GUI_ACTIVE --kernel-trace", PROF_ARGS),
+        "write": ("--pmc WRITE_SIZE SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE --kernel-trace",
+                  PROF_ARGS),
+        "cfetch": ("--pmc FETCH_SIZE", "--copy-calibration-mib 1024"),
+        "cwrite": ("--pmc WRITE_SIZE", "--copy-calibration-mib 1024"),
+    }
+    cmds = {k: cmd.format(opts=o, d=os.path.join(base, k), args=a) for k, (o, a) in runs.items()}
+    mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
+    copy_kib = (1 << 30) / 1024
+    f_scale = mean([v for _, v in _counters(os.path.join(base, "cfetch"), "copyBuffer")["FETCH_SIZE"]]) / copy_kib
+    w_scale = mean([v for _, v in _counters(os.path.join(base, "cwrite"), "copyBuffer")["WRITE_SIZE"]]) / copy_kib
+    cf = _counters(os.path.join(base, "fetch"), "k_lmhead")
+    cw = _counters(os.path.join(base, "write"), "k_lmhead")
+    df = _durations(os.path.join(base, "fetch"), "k_lmhead")
+    dw = _durations(os.path.join(base, "write"), "k_lmhead")
+    kname = next(r["Kernel_Name"] for r in _csv(_one(os.path.join(base, "fetch"),
+                                                     "counter_collection.csv"))
+                 if "k_lmhead" in r["Kernel_Name"])
+    fetch_kib = mean([v for _, v in cf["FETCH_SIZE"]])
+    write_kib = mean([v for _, v in cw["WRITE_SIZE"]])
+    # shader clock: GRBM_GUI_ACTIVE counts GPU cycles per XCD (8 summed) over the dispatch
+    clk = [v / 8.0 / df[i] * 1e3 for i, v in cf["GRBM_GUI_ACTIVE"] if i in df] + \
+          [v / 8.0 / dw[i] * 1e3 for i, v in cw["GRBM_GUI_ACTIVE"] if i in dw]
+    gui = dict(cw["GRBM_GUI_ACTIVE"])
+    busy = [v / (gui[i] / 8.0 * 1024) for i, v in cw["SQ_VALU_MFMA_BUSY_CYCLES"] if i in gui]
+    fb, wb = fetch_kib * 1024 / f_scale, write_kib * 1024 / w_scale
+    alg = 2 * 151936 * 4096 + 2 * 4096 * 4096 + 4 * 4096
+    sclk = mean(clk)
+    text = f"""# LM-head tile kernel, qwen3_8b_head workload (T=4096, H=4096, V=151936, one pass)
+# Per-launch HBM-side traffic, shader clock and MFMA busy from rocprofv3 PMC counters; bytes are
+# scaled by what the same counter reads for a plain 1 GiB device copy (torch copy_, i.e.
+# __amd_rocclr_copyBuffer). Written by: python bench.py --pmc-summary {base}
+#
+# commands (from the repository root, TMPDIR=/tmp):
+""" + "".join(f"#   {cmds[k]}\n" for k in ("fetch", "write", "cfetch", "cwrite")) + f"""kernel: {kname}
+kernel_source_sha256: {kernel_source_sha()}
+dispatches: {len(cf["FETCH_SIZE"])} + {len(cw["WRITE_SIZE"])}
+fetch_size_kib_per_dispatch: {fetch_kib:.1f}
+write_size_kib_per_dispatch: {write_kib:.1f}
+copy_1GiB_fetch_scale: {f_scale:.5f}
+copy_1GiB_write_scale: {w_scale:.5f}
+fetch_bytes_per_launch: {fb:.4g}
+write_bytes_per_launch: {wb:.4g}
+traffic_bytes_per_launch: {fb + wb:.6g}
+algorithmic_bytes_per_launch: {alg:.6g}
+traffic_over_algorithmic: {(fb + wb) / alg:.2f}
+sclk_mhz: {sclk:.0f}
+sclk_mhz_min_max: {min(clk):.0f} {max(clk):.0f}
+mfma_busy_frac: {mean(busy):.4f}
+bf16_peak_at_sclk_tflops: {PEAK_BF16_TFLOPS * sclk / NOMINAL_SCLK_MHZ:.0f}
+"""
+    with open(PROFILE_TRAFFIC, "w") as f:
+        f.write(text)
+    print(text)
+    stats = open(_one(os.path.join(base, "stats"), "kernel_stats.csv")).read()
+    n_lm = len(_durations(os.path.join(base, "stats"), "k_lmhead"))
+    head = f"""# Kernel durations, qwen3_8b_head workload (T=4096, H=4096, V=151936, one pass, 4 vocab segments)
+# command (from the repository root, TMPDIR=/tmp):
+#   {cmds["stats"]}
+# (run_kernel_stats.csv, durations in ns; {n_lm} LM-head calls = warmup + timed steps)
+# kernel_source_sha256: {kernel_source_sha()}
+"""
+    with open(PROFILE_STATS, "w") as f:
+        f.write(head + stats)
+    print(head + stats)
 
 
 def copy_calibration(mib: int) -> None:
@@ -236,6 +360,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-layout-check", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0)
+    ap.add_argument("--pmc-summary", metavar="DIR", default="",
+                    help="write the profiles/ summaries from the rocprofv3 runs under DIR")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the rollout-layout and norm_head measurements")
     args = ap.parse_args()
@@ -246,6 +372,9 @@ def main() -> int:
         return 2
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib)
+        return 0
+    if args.pmc_summary:
+        write_pmc_summary(args.pmc_summary)
         return 0
 
     import numpy as np
@@ -307,11 +436,12 @@ def main() -> int:
     ev.close()
     ms_step = total_ms / args.steps
     kern_ms = float(np.mean(k_ms))
+    k_q = np.percentile(np.asarray(k_ms), [10, 50, 90])
     active = int((y >= 0).sum())
     value = active / (ms_step * 1e-3)
     flops = 2.0 * w.T * w.H * w.V  # every row is computed, padded ones included
     achieved = flops / (kern_ms * 1e-3) / 1e12
-    traffic, traffic_note = committed_traffic()
+    pmc, traffic_note = committed_pmc()
     out_logp = logp.cpu().numpy().copy()
 
     mismatch = None
@@ -340,12 +470,21 @@ def main() -> int:
         "config": {"workload": args.workload, "T": w.T, "H": w.H, "V": w.V,
                    "vocab_segments": w.segments, "layout": "one pass", "parallelism": "none"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic},
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": pmc.get("traffic")},
         "lmhead_kernel_ms": kern_ms,
+        "lmhead_kernel_ms_p10_p50_p90": [float(x) for x in k_q],
         "mfma_util": achieved / PEAK_BF16_TFLOPS,
         "layout_mismatch_count": mismatch,
         "traffic_note": traffic_note,
     }
+    if "sclk_mhz" in pmc:
+        # the published peak assumes 2.4 GHz; under this load the chip's power limit holds the
+        # shader clock lower (measured by the PMC run of the same kernel)
+        peak_clk = PEAK_BF16_TFLOPS * pmc["sclk_mhz"] / NOMINAL_SCLK_MHZ
+        result["sclk_mhz_measured"] = pmc["sclk_mhz"]
+        result["frac_of_peak_at_measured_sclk"] = achieved / peak_clk
+        result["mfma_busy_pmc"] = pmc["mfma_busy"]
     if not args.no_extras:
         log("extras: rollout layout (decode batches x 4 shards), norm_head")
         result["extras"] = extras(rlk, datagen, np, torch, hd, Wd, yd, w, out_logp)
