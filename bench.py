@@ -308,10 +308,50 @@ def time_layout(rlk, lp, hd, Wd, yd, gd, T, steps, warmup, layout_kw, flops_per_
             "lmhead_launches_per_step": n_launch, "_logp": logp.cpu().numpy().copy()}
 
 
+def torch_native(np, torch, hd, Wd, yd, sizes, ref_logp, steps: int = 5, warmup: int = 2) -> dict:
+    """The same rows through a plain framework LM head, for attribution: bf16 logits from the
+    vendor GEMM (``F.linear``, hipBLASLt), then fp32 log_softmax and a gather. Reports its step
+    time, how far it is from this library's output, and whether it keeps its bits when the rows
+    arrive as the rollout's decode batches instead of one pass (each batch its own GEMM)."""
+    h = hd.view(torch.bfloat16)
+    W = Wd.view(torch.bfloat16)
+    y = yd.long()
+    active = y >= 0
+
+    def run(rows: slice):
+        z = torch.nn.functional.linear(h[rows], W).float()
+        lp = torch.log_softmax(z, dim=-1).gather(1, y[rows].clamp_min(0)[:, None])[:, 0]
+        return torch.where(active[rows], lp, torch.zeros_like(lp))
+
+    for _ in range(warmup):
+        run(slice(None))
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        one = run(slice(None))
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    one_h = one.cpu().numpy()
+    offs = np.concatenate([[0], np.cumsum(sizes)])
+    parts = [run(slice(int(offs[i]), int(offs[i + 1]))) for i in range(len(sizes))]
+    torch.cuda.synchronize()
+    dec = torch.cat(parts).cpu().numpy()
+    T = int(h.shape[0])
+    return {"what": "F.linear (bf16 logits) + fp32 log_softmax + gather",
+            "ms_per_step": ms, "tokens_per_s": int(active.sum().item()) / (ms * 1e-3),
+            "mismatch_count_decode_batches_vs_one_pass": int(np.count_nonzero(
+                dec.view(np.uint32) != one_h.view(np.uint32))),
+            "rows": T, "max_abs_diff_vs_this_library": float(np.max(np.abs(
+                one_h.astype(np.float64) - ref_logp.astype(np.float64)))),
+            "_logp": one_h}
+
+
 def extras(rlk, datagen, np, torch, hd, Wd, yd, w, ref_logp) -> dict:
     """The other rows of the path, measured next to the headline: the rollout layout of the TP4
-    workload (decode batches x 4 vocab shards; HBM-bound W stream) and the fused final RMSNorm +
-    temperature + entropy head."""
+    workload (decode batches x 4 vocab shards; HBM-bound W stream), a plain framework LM head on
+    the same rows, and the fused final RMSNorm + temperature + entropy head."""
     out = {}
     lp = rlk.Logprob(w.H, w.V, vocab_segments=w.segments, device=0)
     sizes = datagen.decode_layout(w.T)
@@ -326,6 +366,8 @@ def extras(rlk, datagen, np, torch, hd, Wd, yd, w, ref_logp) -> dict:
         "mismatch_count_vs_one_pass": int(np.count_nonzero(
             r["_logp"].view(np.uint32) != ref_logp.view(np.uint32)))}
     del lp
+    log("extras: torch-native reference path")
+    out["torch_native_lm_head"] = torch_native(np, torch, hd, Wd, yd, sizes, ref_logp)
     wn = datagen.WORKLOADS["norm_head"]
     log("norm_head inputs")
     x = datagen.hidden_bits(wn)
@@ -495,8 +537,14 @@ def main() -> int:
         result["cpu_baseline"] = cb
         result["oracle_max_abs_diff_on_sample"] = float(np.max(np.abs(
             out_logp[rows].astype(np.float64) - ref)))
+        tn = result.get("extras", {}).get("torch_native_lm_head")
+        if tn is not None:
+            tn["max_abs_diff_vs_oracle_on_sample"] = float(np.max(np.abs(
+                tn["_logp"][rows].astype(np.float64) - ref)))
     else:
         result["cpu_baseline"] = None
+    if "torch_native_lm_head" in result.get("extras", {}):
+        result["extras"]["torch_native_lm_head"].pop("_logp")
     print(json.dumps(result), flush=True)
     del keep
     return 0

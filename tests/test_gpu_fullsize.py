@@ -88,6 +88,35 @@ def test_qwen3_head_row_permutation(rlk, head_inputs):
     assert_bitwise(host(a["logp"])[perm], host(b["logp"]), "logp")
 
 
+def test_qwen3_head_stress_hidden_x32(rlk, head_inputs, W64):
+    """Parity-only stress input: the head's hidden scaled by 32 (exact in bf16), so the logits
+    spread ~32x wider (sigma ~2.6 instead of ~0.08) and the tile maxima and EXP arguments cover
+    a much larger range. Sampled oracle parity plus bitwise layouts."""
+    import torch
+
+    w, h, Wb, y, hd, Wd, yd = head_inputs
+    def as_f32(bits):
+        return (bits.astype(np.uint32) << 16).view(np.float32)
+
+    f = as_f32(h) * np.float32(32.0)
+    hs = datagen.f32_to_bf16_bits(f)
+    assert np.array_equal(as_f32(hs), f)  # the scaling is exact
+    hsd = dev_bits(hs)
+    lp = rlk.Logprob(w.H, w.V, vocab_segments=4)
+    say("stress x32: one pass")
+    one = lp.forward(hsd, Wd, yd)
+    torch.cuda.synchronize()
+    got = {k: host(one[k]).copy() for k in ("logp", "lse")}
+    for lay in (dict(row_chunk=1000), dict(vocab_shards=4)):
+        say(f"stress x32: layout {lay}")
+        o = lp.forward(hsd, Wd, yd, **lay)
+        torch.cuda.synchronize()
+        for k in ("logp", "lse"):
+            assert_bitwise(o[k], one[k], (k, str(lay)))
+    assert np.all(got["logp"] <= 0.0) and np.all(np.isfinite(got["logp"]))
+    _parity(got, hs, W64, y, _sample(w.T, 24, y >= 0))
+
+
 def test_tp4_shard_records_merge_equals_unsharded(rlk, head_inputs):
     import torch
 
