@@ -29,6 +29,7 @@
 struct rlk_logprob {
   rlk_logprob_config_t cfg;
   int device;
+  int n_cu;  // compute units of the device
   std::string contract;
 };
 
@@ -82,8 +83,10 @@ rlk_status_t check_config(const rlk_logprob_config_t* c) {
   if (c->vocab_size <= 0 || c->vocab_size % s != 0)
     return fail(RLK_ERR_UNSUPPORTED_SHAPE, "vocab_size %lld is not a positive multiple of %d",
                 (long long)c->vocab_size, s);
-  if (c->vocab_size / s > (1LL << 24))
-    return fail(RLK_ERR_UNSUPPORTED_SHAPE, "vocab segment longer than 2^24");
+  constexpr int64_t kMaxSegLen = (int64_t)rlk::kMaxFoldGroups * rlk::kFoldGroup * rlk::kVocabTile;
+  if (c->vocab_size / s > kMaxSegLen)
+    return fail(RLK_ERR_UNSUPPORTED_SHAPE, "vocab segment of %lld columns is longer than %lld",
+                (long long)(c->vocab_size / s), (long long)kMaxSegLen);
   if (c->vocab_size > 0x7fffffffLL)
     return fail(RLK_ERR_UNSUPPORTED_SHAPE, "vocab_size does not fit int32 targets");
   if (!std::isfinite(c->inv_temperature) || !(c->inv_temperature > 0.0f))
@@ -176,17 +179,6 @@ WsMap ws_map(const rlk_logprob_config_t& c, int64_t rows, int32_t n_tiles, int32
   return m;
 }
 
-// Token tile for a launch of `rows` rows (any choice gives the same bits). Every row tile of a
-// launch streams the whole W range again, so a launch past 128 rows takes the 256-row tile: one
-// 256-row tile of a Qwen3-8B-head vocab segment measured ~105 us against ~145 us for two 128-row
-// tiles. Below that the smaller deep-pipelined tiles keep more W stream in flight per CU.
-int auto_token_tile(int64_t rows) {
-  if (rows > 128) return 256;
-  if (rows > 64) return 128;
-  if (rows > 32) return 64;
-  return 32;
-}
-
 struct DeviceGuard {
   int prev = -1;
   bool changed = false;
@@ -250,9 +242,9 @@ rlk_status_t run_rows(const rlk_logprob* h, const Geometry& g, const void* hidde
   a.seg_begin = s0;
   a.n_seg = s1 - s0;
   a.g_base = g_base;
+  a.n_cu = h->n_cu;
   a.inv_tau = c.inv_temperature;
-  const int bt = token_tile ? token_tile : auto_token_tile(n);
-  hipError_t e = rlk::launch_lmhead(a, bt, ent, st);
+  hipError_t e = rlk::launch_lmhead(a, token_tile, ent, st);
   if (e != hipSuccess) return hip_fail(e, "lm-head launch");
   return RLK_OK;
 }
@@ -305,6 +297,7 @@ RLK_API rlk_status_t rlk_logprob_create(const rlk_logprob_config_t* config, int 
   if (!h) return fail(RLK_ERR_INVALID_ARGUMENT, "out of host memory");
   h->cfg = *config;
   h->device = device;
+  h->n_cu = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
   uint32_t itb;
   std::memcpy(&itb, &config->inv_temperature, 4);
   uint32_t epsb;
@@ -312,11 +305,11 @@ RLK_API rlk_status_t rlk_logprob_create(const rlk_logprob_config_t* config, int 
   char buf[512];
   snprintf(buf, sizeof(buf),
            "rlk-logprob/v%d;mfma=v_mfma_f32_32x32x16_bf16;kstep=16;bv=%d;H=%d;V=%lld;Sc=%d;"
-           "intile=seq16+pair8+half;segfold=seq;segmerge=pair;exp=v_exp_f32(x*0x3fb8aa3b);"
+           "intile=seq16+pair2+half;segfold=seq%d+pair;segmerge=pair;exp=v_exp_f32(x*0x3fb8aa3b);"
            "log=v_log_f32*0x3f317218;inv_tau=0x%08x;rms=%d;rms_eps=0x%08x;rsq=v_rsq_f32;"
            "rms_tree=lane-seq8+xor32..1;entropy=%d;contract=off",
            rlk::kContractVersion, rlk::kVocabTile, config->hidden_size,
-           (long long)config->vocab_size, config->vocab_segments, itb,
+           (long long)config->vocab_size, config->vocab_segments, rlk::kFoldGroup, itb,
            (config->flags & RLK_FLAG_RMSNORM) ? 1 : 0,
            (config->flags & RLK_FLAG_RMSNORM) ? epsb : 0u,
            (config->flags & RLK_FLAG_ENTROPY) ? 1 : 0);

@@ -8,11 +8,15 @@
 
 namespace rlk {
 
-// ---- numeric contract v1 (every constant here decides result bits) ----
-constexpr int kVocabTile = 256;   // BV: vocab tile width, tiles start at each segment's start
-constexpr int kKStage = 64;       // K elements staged per LDS buffer (4 MFMA steps of 16)
+// ---- numeric contract v2 (every constant here decides result bits) ----
+constexpr int kVocabTile = 64;    // BV: vocab tile width, tiles start at each segment's start
+constexpr int kFoldGroup = 32;    // tiles per sequential group of the segment fold
+constexpr int kMaxFoldGroups = 128;  // groups per segment (segments up to 2^18 columns)
 constexpr int kMaxSegments = 8;   // S_c in {1, 2, 4, 8}
-constexpr int kContractVersion = 1;
+constexpr int kContractVersion = 2;
+
+// ---- launch shapes (free: they never change a result bit) ----
+constexpr int kKStage = 64;       // K elements staged per LDS buffer (4 MFMA steps of 16)
 
 // Arguments of the LM-head tile kernel (one launch = a row range x a range of whole segments).
 struct LmheadArgs {
@@ -32,8 +36,12 @@ struct LmheadArgs {
   int32_t seg_begin;        // first segment of this launch
   int32_t n_seg;            // segments in this launch
   int32_t g_base;           // global tile index stored at partial-array row 0
+  int32_t n_cu;             // compute units of the device (picks a launch shape only)
   float inv_tau;
 };
+// A block of the LM-head kernels covers a run of consecutive tiles of one segment (4 tiles,
+// 256 columns, for the MFMA-bound shapes; 3 tiles, 192 columns, for launches of few rows) and
+// a run of rows; each wave of it owns whole tiles, so every tile's reductions stay in one wave.
 
 struct FoldArgs {
   const float* part_m;
@@ -76,7 +84,7 @@ struct RmsArgs {
   float eps;
 };
 
-// Token-tile widths the LM-head kernel is built for.
+// Token-tile widths the LM-head kernel can be forced to (0 = chosen per launch).
 bool token_tile_supported(int bt);
 
 hipError_t launch_lmhead(const LmheadArgs& a, int token_tile, bool entropy, hipStream_t s);

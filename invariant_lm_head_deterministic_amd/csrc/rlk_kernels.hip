@@ -1,6 +1,6 @@
 // HIP kernels of the strict-path selected-token logprob, for gfx950 (MI355X) only.
 //
-// Numeric contract v1. Every result bit of a row is decided by the rules below and by nothing
+// Numeric contract v2. Every result bit of a row is decided by the rules below and by nothing
 // else: not by the row's position in a launch, the launch's row count, the token-tile width,
 // the grid, the number of vocab shards, or which CU or XCD ran a block. The pages ask for a
 // forward whose inputs, split, merge order, precisions, rounding points and primitives are all
@@ -14,22 +14,26 @@
 //     MFMA-based GEMM; K-dim reduction and accumulation precision in the boundary table).
 //  C2 temperature. z' = z * inv_temperature in fp32 (skipped when it is 1.0f: x * 1.0f == x).
 //  C3 vocab split. The vocabulary is S_c contiguous segments of V/S_c; each segment is cut into
-//     tiles of 256 columns from its own start, the last one partial (the "actual vocab range"
+//     tiles of 64 columns from its own start, the last one partial (the "actual vocab range"
 //     and "local reduction" of the "Linear logprob" boundary row).
 //  C4 tile max. m = max of z' over the tile's columns (exact; order-free).
-//  C5 tile sum. e(v) = EXP(z'(v) - m). The tile's 256 columns form 8 blocks of 32 (b = 0..7)
+//  C5 tile sum. e(v) = EXP(z'(v) - m). The tile's 64 columns form 2 blocks of 32 (b = 0, 1)
 //     and two halves h in {0,1}; block b, half h holds the 16 columns
 //     32b + 8(r>>2) + 4h + (r&3), r = 0..15 (the MFMA result-register order). Then
 //        p[b][h] = (((e_r0 + e_r1) + e_r2) + ... ) + e_r15          (sequential in r)
-//        P[h]    = ((p0 + p1) + (p2 + p3)) + ((p4 + p5) + (p6 + p7))  (pairwise in b)
+//        P[h]    = p[0][h] + p[1][h]
 //        s       = P[0] + P[1]
 //     Columns past the end of a partial tile contribute exactly +0. (nxbn.cn blog, §3.2 and
 //     §4.3: sequential sums inside a thread, then a fixed tree; fp32 intermediates.)
 //  C6 entropy term (optional). u uses the same tree with terms e(v) * (z'(v) - m).
 //  C7 target ownership. The one tile whose columns contain y_t writes z'[t, y_t] as computed
 //     in C1-C2 ("target ownership" in the "Linear logprob" boundary row); nothing is summed.
-//  C8 segment fold. M_s = max_j m_j; S_s = sequential sum over tiles j ascending of
-//     s_j * EXP(m_j - M_s); U_s = sequential sum of (u_j + s_j * (m_j - M_s)) * EXP(m_j - M_s).
+//  C8 segment fold. M_s = max_j m_j over the segment's tiles. The tiles form groups of 32
+//     consecutive tiles from the segment start (the last group partial); inside group q
+//        A_q = sequential sum over its tiles j ascending, from +0, of s_j * EXP(m_j - M_s)
+//        B_q = sequential sum, from +0, of (u_j + s_j * (m_j - M_s)) * EXP(m_j - M_s)
+//     and S_s, U_s are balanced pairwise trees over the groups in index order, padded with +0
+//     to a power of two (a pair whose right member is padding passes its left member through).
 //  C9 cross-segment merge. M = max_s M_s; S and U are balanced pairwise trees in segment order
 //     of S_s * EXP(M_s - M) and (U_s + S_s * (M_s - M)) * EXP(M_s - M) (S_c = 4:
 //     (a0 + a1) + (a2 + a3)) — the "cross-rank LSE merge" in a fixed order.
@@ -86,8 +90,21 @@ typedef __attribute__((address_space(3))) void* lptr_t;
 
 // Buffer descriptor over `bytes` bytes from `base` (raw, unstrided; the word-3 value selects
 // 32-bit data format, which makes the descriptor valid for untyped loads).
+// The descriptor must live in SGPRs: its inputs go through readfirstlane (they are uniform by
+// construction) so that the compiler never wraps a DMA in a loop over lanes.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, 0x00020000);
+  const uint64_t b = (uint64_t)base;
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)(uint32_t)b);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)(uint32_t)(b >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc((void*)((hi << 32) | lo), (short)0,
+                                           __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uni64(int64_t x) {
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)(uint32_t)x);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)(uint32_t)((uint64_t)x >> 32));
+  return (int64_t)((hi << 32) | lo);
 }
 
 // Asynchronous 16-byte-per-lane copy global -> LDS (buffer_load_dwordx4 ... lds): lane l's bytes
@@ -112,55 +129,70 @@ __device__ __forceinline__ float tree_sum(const float* v) {
   }
 }
 
-// Where a block's work lies: vocab tile (segment, index in segment, global index, columns) and
-// row tile (first row, rows present).
+// Where a block's work lies: a run of NTPB consecutive vocab tiles of one segment (first global
+// column, columns present, global index of the first tile) and a row tile (first row, rows
+// present).
 struct Tile {
-  int64_t start;  // global vocab index of the tile's first column
-  int len;        // columns in the tile (256, or fewer for a segment's last tile)
-  int g;          // global tile index
+  int64_t start;  // global vocab index of the block's first column
+  int len;        // columns present (64 NTPB, or fewer at a segment's end)
+  int tile0;      // global tile index of the block's first tile
   int row0;       // first launch row of the row tile
   int rows;       // rows present in the row tile
 };
 
-// Block -> (vocab tile, row tile), XCD-aware: consecutive block ids go round-robin to the 8 XCDs,
-// so remap them so that each XCD walks a contiguous range of vocab tiles, a group of 8 vocab
-// tiles at a time across all row tiles (W tiles and hidden tiles shared in L2; 8 was the best of
-// 2, 4, 8, 16 measured on the Qwen3-8B head). Returns false for the few padding blocks.
-template <int BT>
+// Block -> (vocab block, row tile), XCD-aware: consecutive block ids go round-robin to the 8 XCDs,
+// so remap them so that each XCD walks a contiguous range of vocab blocks, a group of 8 vocab
+// blocks at a time across all row tiles (W and hidden tiles shared in L2; 8 was the best of 2,
+// 4, 8, 16 measured on the Qwen3-8B head). Returns false for the few padding blocks.
+template <int BT, int NTPB>
 __device__ __forceinline__ bool map_tile(const LmheadArgs& a, Tile& t) {
-  const int n_vt = a.n_seg * a.tiles_per_seg;
+  const int bps = (a.tiles_per_seg + NTPB - 1) / NTPB;  // vocab blocks per segment
+  const int n_vb = a.n_seg * bps;
   const int n_tt = (a.rows + BT - 1) / BT;
-  const int64_t n_items = (int64_t)n_vt * n_tt;
+  const int64_t n_items = (int64_t)n_vb * n_tt;
   const int64_t per_xcd = (int64_t)gridDim.x / 8;
   const int64_t L = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
   if (L >= n_items) return false;
   constexpr int GV = 8;
   const int64_t grp = L / ((int64_t)GV * n_tt);
   const int first_v = (int)(grp * GV);
-  const int gsz = min(GV, n_vt - first_v);
+  const int gsz = min(GV, n_vb - first_v);
   const int64_t within = L - grp * GV * n_tt;
-  const int vt = first_v + (int)(within % gsz);
+  const int vb = first_v + (int)(within % gsz);
   const int tt = (int)(within / gsz);
-  const int seg = a.seg_begin + vt / a.tiles_per_seg;
-  const int jt = vt % a.tiles_per_seg;
-  t.start = (int64_t)seg * a.seg_len + (int64_t)jt * kVocabTile;
-  t.len = (int)min((int64_t)kVocabTile, a.seg_len - (int64_t)jt * kVocabTile);
-  t.g = seg * a.tiles_per_seg + jt;
-  t.row0 = tt * BT;
-  t.rows = min(BT, a.rows - t.row0);
+  const int seg = a.seg_begin + vb / bps;
+  const int jb = vb % bps;
+  const int64_t col0 = (int64_t)jb * NTPB * kVocabTile;
+  // all of it depends on blockIdx only; readfirstlane states that to the compiler
+  t.start = uni64((int64_t)seg * a.seg_len + col0);
+  t.len = uni((int)min((int64_t)NTPB * kVocabTile, a.seg_len - col0));
+  t.tile0 = uni(seg * a.tiles_per_seg + jb * NTPB);
+  t.row0 = uni(tt * BT);
+  t.rows = uni(min(BT, a.rows - tt * BT));
   return true;
 }
 
-// Fused tile epilogue (C2, C4-C7) on the MFMA result registers of one wave. The wave owns
-// VB = 8 / VW of the tile's 32-column blocks (wave index wv) and NTB row blocks of 32 (row block
-// wt * NTB + j). For VW > 1 the tile max and the upper levels of the sum tree cross waves through
-// LDS (red_m [VW][BT], red_s and red_u [VW][2][BT]); every wave of the block must call this.
-template <int VW, int TW, int NTB, bool ENT, bool TEMP>
-__device__ __forceinline__ void tile_epilogue(f32x16 (&acc)[8 / VW][NTB], const LmheadArgs& a,
-                                              const Tile& t, int wv, int wt, int half, int col,
-                                              float* red_m, float* red_s, float* red_u) {
-  constexpr int VB = 8 / VW;
-  constexpr int BT = 32 * NTB * TW;
+// Fused tile epilogue (C2, C4-C7) on the MFMA result registers of one wave. The wave owns VB
+// column blocks of 32 (block columns 32 VB wv ..), i.e. VB/2 whole tiles, and NTB row blocks of
+// 32 (rows 32 (wt NTB + j) ..), so every reduction of a tile stays inside the wave: lane-local
+// sums plus one exchange between the two lane halves.
+// Target of this lane's row in row block j (-1 past the row tile), read before the K loop so that
+// its latency hides behind the MFMAs.
+template <int NTB>
+__device__ __forceinline__ void load_targets(int (&y)[NTB], const LmheadArgs& a, const Tile& t,
+                                             int wt, int col) {
+#pragma unroll
+  for (int j = 0; j < NTB; ++j) {
+    const int rr = 32 * (wt * NTB + j) + col;
+    y[j] = rr < t.rows ? a.targets[t.row0 + rr] : -1;
+  }
+}
+
+template <int VB, int NTB, bool ENT, bool TEMP>
+__device__ __forceinline__ void tile_epilogue(f32x16 (&acc)[VB][NTB], const int (&ytgt)[NTB],
+                                              const LmheadArgs& a, const Tile& t, int wv, int wt,
+                                              int half, int col) {
+  static_assert(VB % 2 == 0, "a wave owns whole tiles");
   if constexpr (TEMP) {
 #pragma unroll
     for (int i = 0; i < VB; ++i)
@@ -169,124 +201,78 @@ __device__ __forceinline__ void tile_epilogue(f32x16 (&acc)[8 / VW][NTB], const 
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = acc[i][j][r] * a.inv_tau;
   }
-  const bool partial = t.len < kVocabTile;
-  const int tile_len = t.len;
-  // column offset inside the tile of (block i, register r) for this lane
-  auto coff = [&](int i, int r) { return 32 * (wv * VB + i) + 8 * (r >> 2) + 4 * half + (r & 3); };
-
-  float m[NTB];
+  // column offset inside a tile of (block b of the tile, register r) for this lane
+  auto coff = [&](int b, int r) { return 32 * b + 8 * (r >> 2) + 4 * half + (r & 3); };
 #pragma unroll
-  for (int j = 0; j < NTB; ++j) {
-    float mm = -INFINITY;
-    if (partial) {
-#pragma unroll
-      for (int i = 0; i < VB; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (coff(i, r) < tile_len) mm = fmaxf(mm, acc[i][j][r]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < VB; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mm = fmaxf(mm, acc[i][j][r]);
-    }
-    m[j] = fmaxf(mm, __shfl_xor(mm, 32));
-  }
-  if constexpr (VW > 1) {
-#pragma unroll
-    for (int j = 0; j < NTB; ++j)
-      if (half == 0) red_m[wv * BT + 32 * (wt * NTB + j) + col] = m[j];
-    __syncthreads();
+  for (int c = 0; c < VB / 2; ++c) {
+    const int tc = wv * (VB / 2) + c;  // tile index inside the block
+    const int tlen = min(kVocabTile, t.len - tc * kVocabTile);
+    if (tlen <= 0) continue;  // past the segment's end (uniform across the wave)
+    const bool partial = tlen < kVocabTile;
+    const int64_t go = (int64_t)(t.tile0 + tc - a.g_base) * a.ld;
+    const int64_t tstart = t.start + (int64_t)tc * kVocabTile;
 #pragma unroll
     for (int j = 0; j < NTB; ++j) {
-      float mm = red_m[32 * (wt * NTB + j) + col];
-#pragma unroll
-      for (int w = 1; w < VW; ++w) mm = fmaxf(mm, red_m[w * BT + 32 * (wt * NTB + j) + col]);
-      m[j] = mm;
-    }
-  }
-
-  float qs[NTB], qu[NTB];
-#pragma unroll
-  for (int j = 0; j < NTB; ++j) {
-    float p[VB], pu[VB];
-#pragma unroll
-    for (int i = 0; i < VB; ++i) {
-      float ps = 0.0f, pq = 0.0f;
+      const f32x16& z0 = acc[2 * c][j];
+      const f32x16& z1 = acc[2 * c + 1][j];
+      float mm = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float d = acc[i][j][r] - m[j];
-        float e = c_exp(d);
-        if (partial && coff(i, r) >= tile_len) e = 0.0f;
-        ps = ps + e;
-        if constexpr (ENT) {
-          float q = e * d;
-          if (partial && coff(i, r) >= tile_len) q = 0.0f;
-          pq = pq + q;
+        if (!partial || coff(0, r) < tlen) mm = fmaxf(mm, z0[r]);
+        if (!partial || coff(1, r) < tlen) mm = fmaxf(mm, z1[r]);
+      }
+      const float m = fmaxf(mm, __shfl_xor(mm, 32));
+      float p[2], pu[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const f32x16& z = b ? z1 : z0;
+        float ps = 0.0f, pq = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float d = z[r] - m;
+          float e = c_exp(d);
+          const bool out = partial && coff(b, r) >= tlen;
+          if (out) e = 0.0f;
+          ps = ps + e;
+          if constexpr (ENT) {
+            float q = e * d;
+            if (out) q = 0.0f;
+            pq = pq + q;
+          }
         }
+        p[b] = ps;
+        pu[b] = pq;
       }
-      p[i] = ps;
-      pu[i] = pq;
-    }
-    qs[j] = tree_sum<VB>(p);
-    if constexpr (ENT) qu[j] = tree_sum<VB>(pu);
-  }
-
-  if constexpr (VW > 1) {
-#pragma unroll
-    for (int j = 0; j < NTB; ++j) {
-      red_s[(wv * 2 + half) * BT + 32 * (wt * NTB + j) + col] = qs[j];
-      if constexpr (ENT) red_u[(wv * 2 + half) * BT + 32 * (wt * NTB + j) + col] = qu[j];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < NTB; ++j) {
-      float v[VW], vu[VW];
-#pragma unroll
-      for (int w = 0; w < VW; ++w) {
-        v[w] = red_s[(w * 2 + half) * BT + 32 * (wt * NTB + j) + col];
-        if constexpr (ENT) vu[w] = red_u[(w * 2 + half) * BT + 32 * (wt * NTB + j) + col];
+      const float P = p[0] + p[1];
+      const float sum = P + __shfl_xor(P, 32);  // P[0] + P[1] on both halves (commutative)
+      float u = 0.0f;
+      if constexpr (ENT) {
+        const float PU = pu[0] + pu[1];
+        u = PU + __shfl_xor(PU, 32);
       }
-      qs[j] = tree_sum<VW>(v);
-      if constexpr (ENT) qu[j] = tree_sum<VW>(vu);
-    }
-  }
-
-  // halves: s = P[0] + P[1] (fp32 addition is commutative, so both lanes agree)
-  float* __restrict__ pm = a.part_m + (int64_t)(t.g - a.g_base) * a.ld;
-  float* __restrict__ psum = a.part_s + (int64_t)(t.g - a.g_base) * a.ld;
+      const int rr = 32 * (wt * NTB + j) + col;  // row inside the row tile
+      if (half == 0 && rr < t.rows) {
+        const int64_t row = (int64_t)t.row0 + rr;
+        a.part_m[go + row] = m;
+        a.part_s[go + row] = sum;
+        if constexpr (ENT) a.part_u[go + row] = u;
+      }
+      // target ownership: the lane whose registers hold column y_t of this tile writes z'[t, y_t]
+      const int y = ytgt[j];
+      const int64_t d = (int64_t)y - tstart;
+      const bool in_tile = y >= 0 && d >= 0 && d < tlen;
+      const int dd = (int)d;
+      const bool mine = in_tile && (((dd >> 2) & 1) == half);
+      if (__any(mine)) {
+        const int ridx = (dd >> 5) * 16 + ((dd >> 3) & 3) * 4 + (dd & 3);
+        float v = 0.0f;
 #pragma unroll
-  for (int j = 0; j < NTB; ++j) {
-    const float sum = qs[j] + __shfl_xor(qs[j], 32);
-    float u = 0.0f;
-    if constexpr (ENT) u = qu[j] + __shfl_xor(qu[j], 32);
-    const int rr = 32 * (wt * NTB + j) + col;  // row inside the row tile
-    if (wv == 0 && half == 0 && rr < t.rows) {
-      const int64_t row = (int64_t)t.row0 + rr;
-      pm[row] = m[j];
-      psum[row] = sum;
-      if constexpr (ENT) a.part_u[(int64_t)(t.g - a.g_base) * a.ld + row] = u;
-    }
-  }
-
-  // target ownership: the lane whose registers hold column y_t of this tile writes z'[t, y_t]
-#pragma unroll
-  for (int j = 0; j < NTB; ++j) {
-    const int rr = 32 * (wt * NTB + j) + col;
-    int y = -1;
-    if (rr < t.rows) y = a.targets[t.row0 + rr];
-    const int64_t d = (int64_t)y - t.start;
-    const bool in_tile = y >= 0 && d >= 0 && d < tile_len;
-    const int dd = (int)d;
-    const bool mine = in_tile && ((dd >> 5) / VB == wv) && (((dd >> 2) & 1) == half);
-    if (__any(mine)) {
-      const int ridx = ((dd >> 5) % VB) * 16 + ((dd >> 3) & 3) * 4 + (dd & 3);
-      float v = 0.0f;
-#pragma unroll
-      for (int i = 0; i < VB; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) v = (i * 16 + r == ridx) ? acc[i][j][r] : v;
-      if (mine) a.tgt[t.row0 + rr] = v;
+        for (int r = 0; r < 16; ++r) {
+          v = (r == ridx) ? z0[r] : v;
+          v = (16 + r == ridx) ? z1[r] : v;
+        }
+        if (mine) a.tgt[t.row0 + rr] = v;
+      }
     }
   }
 }
@@ -304,24 +290,25 @@ k_lmhead(const LmheadArgs a) {
   constexpr int NWAVES = VW * TW;
   constexpr int NT = 64 * NWAVES;
   constexpr int BT = 32 * NTB * TW;
-  constexpr int VB = 8 / VW;
-  constexpr int WI = kVocabTile / 8 / NWAVES;  // DMA instructions per wave per W stage
+  constexpr int BW = 4 * kVocabTile;          // block columns: 4 tiles
+  constexpr int VB = BW / 32 / VW;
+  constexpr int WI = BW / 8 / NWAVES;          // DMA instructions per wave per W stage
   constexpr int HI = BT / 8 / NWAVES;          // DMA instructions per wave per hidden stage
-  static_assert(VB * VW == 8 && WI * 8 * NWAVES == kVocabTile && HI * 8 * NWAVES == BT, "tiling");
+  static_assert(VB * VW * 32 == BW && WI * 8 * NWAVES == BW && HI * 8 * NWAVES == BT, "tiling");
   (void)NT;
 
   // two stages as distinct objects, so the compiler can tell a DMA into one stage from reads
   // of the other and does not wait for the DMA before those reads
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_w0[kVocabTile * kRowBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_w1[kVocabTile * kRowBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_w0[BW * kRowBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_w1[BW * kRowBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_h0[BT * kRowBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_h1[BT * kRowBytes];
-  __shared__ float red_m[(VW > 1 ? VW : 1) * BT];
-  __shared__ float red_s[(VW > 1 ? VW : 1) * 2 * BT];
-  __shared__ float red_u[(VW > 1 && ENT ? VW : 1) * 2 * BT];
 
   Tile t;
-  if (!map_tile<BT>(a, t)) return;
+  if (!map_tile<BT, 4>(a, t)) return;
+  int ytgt[NTB];
+  load_targets<NTB>(ytgt, a, t, (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) / VW,
+                    threadIdx.x & 31);
   const int64_t tile_start = t.start;
   const int tile_len = t.len;
   const int row0 = t.row0;
@@ -469,15 +456,16 @@ k_lmhead(const LmheadArgs a) {
   stage(std::false_type{}, k, lds_w0, lds_h0, lds_w1, lds_h1);
   stage(std::false_type{}, k + 1, lds_w1, lds_h1, lds_w0, lds_h0);
 
-  tile_epilogue<VW, TW, NTB, ENT, TEMP>(acc, a, t, wv, wt, half, col, red_m, red_s, red_u);
+  tile_epilogue<VB, NTB, ENT, TEMP>(acc, ytgt, a, t, wv, wt, half, col);
 }
 
 // --------------------------------------------------------------------------------------------
-// K1d: deep-pipeline LM-head tile kernel for launches of few rows (decode batches). Same tiles,
-// same MFMA chain (C1), same fragment order and the same epilogue as k_lmhead, hence the same
-// bits; only the staging depth differs. A decode batch has one or two row tiles, so a launch
-// has few blocks and the W stream is bound by the bytes each block keeps in flight: these
-// variants cycle NS (3-4) LDS stages, so NS-1 stages of DMA are outstanding while one is read.
+// K1d: deep-pipeline LM-head tile kernel for launches of few rows (decode batches). Same MFMA
+// chain (C1), same fragment order and the same per-tile epilogue as k_lmhead, hence the same
+// bits; only the staging depth and the block shape (NTPB = 3 or 4 tiles) differ. A decode
+// batch has one row tile, so a launch has few blocks and the W stream is bound by the bytes
+// each block keeps in flight: these variants cycle NS (2-4) LDS stages, so NS-1 stages of DMA
+// are outstanding while one is read.
 // The stage buffer is picked at run time; the DMA is issued from inline assembly so that the
 // compiler, which cannot tell the stage buffers apart at run time, does not wait for every
 // outstanding DMA before each LDS read. Its completion is awaited explicitly (vmcnt) before the
@@ -488,10 +476,12 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 // Raw buffer descriptor (base, unstrided, `bytes` long, 32-bit data format) in 4 SGPRs.
 __device__ __forceinline__ i32x4 buffer_desc(const void* base, uint32_t bytes) {
   const uint64_t b = (uint64_t)base;
+  // the descriptor is uniform by construction; readfirstlane keeps it in SGPRs, which the
+  // inline assembly below requires
   i32x4 d;
-  d[0] = (int32_t)(uint32_t)b;
-  d[1] = (int32_t)((uint32_t)(b >> 32) & 0xffffu);
-  d[2] = (int32_t)bytes;
+  d[0] = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)b);
+  d[1] = __builtin_amdgcn_readfirstlane((int32_t)((uint32_t)(b >> 32) & 0xffffu));
+  d[2] = __builtin_amdgcn_readfirstlane((int32_t)bytes);
   d[3] = 0x00020000;
   return d;
 }
@@ -510,27 +500,31 @@ __device__ __forceinline__ void wait_vm() {
   __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(D) : "memory");
 }
 
-template <int VW, int TW, int NTB, int NS, bool ENT, bool TEMP>
+template <int VW, int TW, int NTB, int NS, int NTPB, bool ENT, bool TEMP>
 __global__ void __launch_bounds__(64 * VW * TW) k_lmhead_deep(const LmheadArgs a) {
   constexpr int NWAVES = VW * TW;
   constexpr int BT = 32 * NTB * TW;
-  constexpr int VB = 8 / VW;
-  constexpr int WI = kVocabTile / 8 / NWAVES;
-  constexpr int HI = BT / 8 / NWAVES;
+  constexpr int BW = NTPB * kVocabTile;  // block columns
+  constexpr int VB = BW / 32 / VW;
+  constexpr int WI = BW / 8 / NWAVES;
+  // hidden rows are staged in whole DMA rounds of 8 NWAVES rows; rows past BT repeat the last
+  // row and are never read
+  constexpr int HI = (BT / 8 + NWAVES - 1) / NWAVES;
   constexpr int DPS = WI + HI;  // DMA instructions per wave per stage
-  constexpr int SW = kVocabTile * kRowBytes;
-  constexpr int SH = BT * kRowBytes;
-  static_assert(VB * VW == 8 && WI * 8 * NWAVES == kVocabTile && HI * 8 * NWAVES == BT, "tiling");
+  constexpr int SW = BW * kRowBytes;
+  constexpr int SH = 8 * HI * NWAVES * kRowBytes;
+  static_assert(VB * VW * 32 == BW && VB % 2 == 0 && WI * 8 * NWAVES == BW && BT % 32 == 0,
+                "tiling");
   static_assert(NS >= 2 && NS <= 4 && (NS - 2) * DPS <= 63, "stages");
 
   __shared__ __attribute__((aligned(1024))) uint8_t lds_w[NS * SW];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_h[NS * SH];
-  __shared__ float red_m[(VW > 1 ? VW : 1) * BT];
-  __shared__ float red_s[(VW > 1 ? VW : 1) * 2 * BT];
-  __shared__ float red_u[(VW > 1 && ENT ? VW : 1) * 2 * BT];
 
   Tile t;
-  if (!map_tile<BT>(a, t)) return;
+  if (!map_tile<BT, NTPB>(a, t)) return;
+  int ytgt[NTB];
+  load_targets<NTB>(ytgt, a, t, (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) / VW,
+                    threadIdx.x & 31);
   const int H = a.H;
   const uint16_t* __restrict__ Wt = a.W + (t.start - a.w_row0) * (int64_t)H;
   const uint16_t* __restrict__ Ht = a.hidden + (int64_t)t.row0 * H;
@@ -637,62 +631,98 @@ __global__ void __launch_bounds__(64 * VW * TW) k_lmhead_deep(const LmheadArgs a
   }
   wait_vm<0>();
 
-  tile_epilogue<VW, TW, NTB, ENT, TEMP>(acc, a, t, wv, wt, half, col, red_m, red_s, red_u);
+  tile_epilogue<VB, NTB, ENT, TEMP>(acc, ytgt, a, t, wv, wt, half, col);
 }
 
 // --------------------------------------------------------------------------------------------
-// K2a: per (row, segment) fold of the segment's tile partials (C8).
+// K2a: fold of one segment's tile partials for 64 rows (C8). Lane = row, so every load of a wave
+// is one contiguous 256-byte piece of a [tile][row] array. The block's 16 waves first take the
+// segment's tiles round-robin for the exact maximum, then its groups of 32 tiles round-robin,
+// each group one sequential chain; wave 0 then runs the pairwise tree over the groups in LDS.
 // --------------------------------------------------------------------------------------------
+constexpr int kFoldWaves = 16;
+
 template <bool ENT>
-__global__ void __launch_bounds__(256) k_segment_fold(const FoldArgs a) {
-  // The fold is one sequential chain per (row, segment) by contract; its loads do not depend on
-  // the chain, so they are issued in batches of U ahead of the arithmetic.
-  constexpr int U = 16;
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t >= a.rows) return;
-  const int sl = blockIdx.y;
+__global__ void __launch_bounds__(64 * kFoldWaves) k_segment_fold(const FoldArgs a) {
+  constexpr int G = kFoldGroup;
+  constexpr int U = 8;  // loads issued ahead of the arithmetic
+  __shared__ float red[kFoldWaves][64];
+  __shared__ float ga[kMaxFoldGroups][64];
+  __shared__ float gb[ENT ? kMaxFoldGroups : 1][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int t = blockIdx.x * 64 + lane;
+  const bool live = t < a.rows;
+  const int sl = blockIdx.y;  // segment inside this launch's range
   const int seg = a.seg_begin + sl;
   const int64_t g0 = (int64_t)seg * a.tiles_per_seg - a.g_base;
-  const float* __restrict__ pm = a.part_m + g0 * a.ld + t;
-  const float* __restrict__ ps = a.part_s + g0 * a.ld + t;
-  const float* __restrict__ pu = ENT ? a.part_u + g0 * a.ld + t : nullptr;
+  const int64_t tc = live ? t : 0;  // dead lanes read row 0 (in bounds) and write nothing
+  const float* __restrict__ pm = a.part_m + g0 * a.ld + tc;
+  const float* __restrict__ ps = a.part_s + g0 * a.ld + tc;
+  const float* __restrict__ pu = ENT ? a.part_u + g0 * a.ld + tc : nullptr;
   const int n = a.tiles_per_seg;
+  const int Q = (n + G - 1) / G;
+
   float M = -INFINITY;
-  for (int j0 = 0; j0 < n; j0 += U) {
+  for (int j0 = wave; j0 < n; j0 += U * kFoldWaves) {
     float v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = (j0 + u < n) ? pm[(int64_t)(j0 + u) * a.ld] : -INFINITY;
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + u * kFoldWaves;
+      v[u] = j < n ? pm[(int64_t)j * a.ld] : -INFINITY;
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) M = fmaxf(M, v[u]);
   }
-  float S = 0.0f, U_ = 0.0f;
-  for (int j0 = 0; j0 < n; j0 += U) {
-    float vm[U], vs[U], vu[U];
+  red[wave][lane] = M;
+  __syncthreads();
+  M = red[0][lane];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const bool in = j0 + u < n;
-      const int64_t o = (int64_t)(j0 + u) * a.ld;
-      vm[u] = in ? pm[o] : 0.0f;
-      vs[u] = in ? ps[o] : 0.0f;
-      if constexpr (ENT) vu[u] = in ? pu[o] : 0.0f;
-    }
+  for (int w = 1; w < kFoldWaves; ++w) M = fmaxf(M, red[w][lane]);
+
+  for (int q = wave; q < Q; q += kFoldWaves) {
+    const int j1 = min(n, (q + 1) * G);
+    float A = 0.0f, B = 0.0f;
+    for (int j0 = q * G; j0 < j1; j0 += U) {
+      float vm[U], vs[U], vu[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (j0 + u < n) {
-        const float dm = vm[u] - M;
-        const float e = c_exp(dm);
-        S = S + vs[u] * e;
-        if constexpr (ENT) U_ = U_ + (vu[u] + vs[u] * dm) * e;
+      for (int u = 0; u < U; ++u) {
+        const bool in = j0 + u < j1;
+        const int64_t o = (int64_t)(j0 + u) * a.ld;
+        vm[u] = in ? pm[o] : 0.0f;
+        vs[u] = in ? ps[o] : 0.0f;
+        if constexpr (ENT) vu[u] = in ? pu[o] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (j0 + u < j1) {
+          const float dm = vm[u] - M;
+          const float e = c_exp(dm);
+          A = A + vs[u] * e;
+          if constexpr (ENT) B = B + (vu[u] + vs[u] * dm) * e;
+        }
       }
     }
+    ga[q][lane] = A;
+    if constexpr (ENT) gb[q][lane] = B;
   }
+  __syncthreads();
+  if (wave != 0) return;
+  // pairwise tree over the groups in index order; a missing right member passes the left through
+  for (int st = 1; st < Q; st *= 2) {
+    for (int q = 0; q + st < Q; q += 2 * st) {
+      ga[q][lane] = ga[q][lane] + ga[q + st][lane];
+      if constexpr (ENT) gb[q][lane] = gb[q][lane] + gb[q + st][lane];
+    }
+  }
+  if (!live) return;
   const int32_t y = a.targets[t];
   const int64_t lo = (int64_t)seg * a.seg_len;
   const bool owner = y >= 0 && (int64_t)y >= lo && (int64_t)y < lo + a.seg_len;
   rlk_segment_record_t r;
   r.m = M;
-  r.s = S;
-  r.u = ENT ? U_ : 0.0f;
+  r.s = ga[0][lane];
+  r.u = ENT ? gb[0][lane] : 0.0f;
   r.tgt = owner ? a.tgt[t] : __builtin_nanf("");
   a.rec[(int64_t)sl * a.rec_ld + t] = r;
 }
@@ -812,14 +842,20 @@ __global__ void k_clear_status(uint32_t* status) {
 // --------------------------------------------------------------------------------------------
 bool token_tile_supported(int bt) { return bt == 32 || bt == 64 || bt == 128 || bt == 256; }
 
+// Blocks of a launch: vocab blocks of NTPB tiles per segment x row tiles, rounded up to a
+// multiple of 8 (the XCD remap in map_tile; the extra blocks exit at once).
+template <int BT, int NTPB>
+static int64_t lmhead_blocks(const LmheadArgs& a) {
+  const int64_t n_vb = (int64_t)a.n_seg * ((a.tiles_per_seg + NTPB - 1) / NTPB);
+  const int64_t n_tt = (a.rows + BT - 1) / BT;
+  return (n_vb * n_tt + 7) / 8 * 8;
+}
+
 template <int VW, int TW, int NTB>
 static hipError_t launch_variant(const LmheadArgs& a, bool ent, hipStream_t s) {
   constexpr int BT = 32 * NTB * TW;
-  const int64_t n_vt = (int64_t)a.n_seg * a.tiles_per_seg;
-  const int64_t n_tt = (a.rows + BT - 1) / BT;
-  const int64_t items = n_vt * n_tt;
-  const int64_t blocks = (items + 7) / 8 * 8;
-  if (items == 0) return hipSuccess;
+  const int64_t blocks = lmhead_blocks<BT, 4>(a);
+  if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)blocks), block(64 * VW * TW);
   const bool temp = a.inv_tau != 1.0f;
@@ -833,40 +869,62 @@ static hipError_t launch_variant(const LmheadArgs& a, bool ent, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int VW, int TW, int NTB, int NS>
+template <int VW, int TW, int NTB, int NS, int NTPB>
 static hipError_t launch_deep(const LmheadArgs& a, bool ent, hipStream_t s) {
   constexpr int BT = 32 * NTB * TW;
-  const int64_t n_vt = (int64_t)a.n_seg * a.tiles_per_seg;
-  const int64_t n_tt = (a.rows + BT - 1) / BT;
-  const int64_t items = n_vt * n_tt;
-  const int64_t blocks = (items + 7) / 8 * 8;
-  if (items == 0) return hipSuccess;
+  const int64_t blocks = lmhead_blocks<BT, NTPB>(a);
+  if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)blocks), block(64 * VW * TW);
   const bool temp = a.inv_tau != 1.0f;
   if (ent) {
-    if (temp) hipLaunchKernelGGL((k_lmhead_deep<VW, TW, NTB, NS, true, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_lmhead_deep<VW, TW, NTB, NS, true, false>), grid, block, 0, s, a);
+    if (temp) hipLaunchKernelGGL((k_lmhead_deep<VW, TW, NTB, NS, NTPB, true, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_lmhead_deep<VW, TW, NTB, NS, NTPB, true, false>), grid, block, 0, s, a);
   } else {
-    if (temp) hipLaunchKernelGGL((k_lmhead_deep<VW, TW, NTB, NS, false, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_lmhead_deep<VW, TW, NTB, NS, false, false>), grid, block, 0, s, a);
+    if (temp) hipLaunchKernelGGL((k_lmhead_deep<VW, TW, NTB, NS, NTPB, false, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_lmhead_deep<VW, TW, NTB, NS, NTPB, false, false>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }
 
+// Launch shape for token_tile 0 (every choice gives the same bits). Launches past 256 rows take
+// the 256-row tile of k_lmhead. Up to 256 rows (decode batches) there is one row tile, and the
+// launch is bound by how many columns its busiest CU streams and multiplies: blocks of 3 tiles
+// (192 columns) spread a Qwen3-8B vocab segment over 198 blocks instead of 149, so they are taken
+// whenever they put fewer columns on the busiest CU than blocks of 4 tiles do, with row tiles of
+// 64 to 256 rows (never more than 63 rows of padding). token_tile 32/64/128/256 forces blocks of
+// 4 tiles with that row tile.
+static bool three_tile_blocks(const LmheadArgs& a) {
+  const int64_t cu = a.n_cu > 0 ? a.n_cu : 256;
+  const int64_t n3 = (int64_t)a.n_seg * ((a.tiles_per_seg + 2) / 3);
+  const int64_t n4 = (int64_t)a.n_seg * ((a.tiles_per_seg + 3) / 4);
+  return (n3 + cu - 1) / cu * 3 < (n4 + cu - 1) / cu * 4;
+}
+
 hipError_t launch_lmhead(const LmheadArgs& a, int bt, bool ent, hipStream_t s) {
+  if (bt == 0) {
+    if (a.rows > 256) return launch_variant<2, 4, 2>(a, ent, s);
+    if (three_tile_blocks(a)) {
+      if (a.rows > 192) return launch_deep<3, 4, 2, 2, 3>(a, ent, s);
+      if (a.rows > 128) return launch_deep<3, 2, 3, 3, 3>(a, ent, s);
+      if (a.rows > 64) return launch_deep<3, 2, 2, 3, 3>(a, ent, s);
+      return launch_deep<3, 2, 1, 3, 3>(a, ent, s);
+    }
+    bt = a.rows > 128 ? 256 : a.rows > 64 ? 128 : a.rows > 32 ? 64 : 32;
+  }
   switch (bt) {
     case 256: return launch_variant<2, 4, 2>(a, ent, s);
-    case 128: return launch_deep<2, 2, 2, 3>(a, ent, s);
-    case 64: return launch_deep<4, 1, 2, 3>(a, ent, s);
-    case 32: return launch_deep<4, 1, 1, 4>(a, ent, s);
+    case 128: return launch_deep<2, 2, 2, 3, 4>(a, ent, s);
+    case 64: return launch_deep<4, 1, 2, 3, 4>(a, ent, s);
+    case 32: return launch_deep<4, 1, 1, 4, 4>(a, ent, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_fold(const FoldArgs& a, bool ent, hipStream_t s) {
   if (a.rows == 0 || a.n_seg == 0) return hipSuccess;
-  const dim3 grid((unsigned)((a.rows + 255) / 256), (unsigned)a.n_seg), block(256);
+  if ((a.tiles_per_seg + kFoldGroup - 1) / kFoldGroup > kMaxFoldGroups) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((a.rows + 63) / 64), (unsigned)a.n_seg), block(64 * kFoldWaves);
   if (ent) hipLaunchKernelGGL(k_segment_fold<true>, grid, block, 0, s, a);
   else hipLaunchKernelGGL(k_segment_fold<false>, grid, block, 0, s, a);
   return hipGetLastError();

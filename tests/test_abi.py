@@ -46,7 +46,7 @@ def test_workspace_size_matches_the_partial_arrays(lib):
     cfg = make_config(4096, 151936)
     layout, _k = make_layout(4096)
     n = _ws(cfg, layout)
-    tiles = 4 * 149  # 37984 = 148 * 256 + 96
+    tiles = 4 * 594  # 37984 = 593 * 64 + 32
     want = 256 + 4096 * 4 + 2 * tiles * 4096 * 4 + 4 * 4096 * 16
     assert want <= n <= want + 8 * 256
     cfg_e = make_config(4096, 151936, entropy=True)
@@ -79,6 +79,8 @@ def test_layout_check_counts_launches(lib):
     (dict(hidden_size=256, vocab_size=1000, vocab_segments=3), _lib.RLK_ERR_UNSUPPORTED_SHAPE),
     (dict(hidden_size=256, vocab_size=1000, vocab_segments=16), _lib.RLK_ERR_UNSUPPORTED_SHAPE),
     (dict(hidden_size=0, vocab_size=1000), _lib.RLK_ERR_UNSUPPORTED_SHAPE),
+    # a segment longer than the fold's 128 groups of 32 tiles of 64 columns
+    (dict(hidden_size=128, vocab_size=262145 * 2, vocab_segments=2), _lib.RLK_ERR_UNSUPPORTED_SHAPE),
 ])
 def test_bad_configs_are_rejected(lib, kw, status):
     cfg = make_config(**kw)
@@ -118,6 +120,17 @@ def test_temperature_and_nan_config(lib):
     assert e.value.status == _lib.RLK_ERR_INVALID_ARGUMENT
     c = make_config(256, 1000, temperature=0.7)
     assert ctypes.c_float(c.inv_temperature).value == pytest.approx(1 / 0.7, rel=1e-7)
+
+
+def test_longest_segment_is_accepted(lib):
+    cfg = make_config(128, 262144 * 4, vocab_segments=4)
+    l, _k = make_layout(8)
+    assert _ws(cfg, l) > 0
+
+
+def test_contract_id_names_the_tile_and_fold(lib):
+    fp = _lib.rlk_build_fingerprint()
+    assert "contract v2" in fp
 
 
 def test_partials_range_must_sit_on_segment_boundaries(lib):

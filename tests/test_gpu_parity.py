@@ -53,12 +53,16 @@ def test_tiny_workload_matches_oracle(rlk):
 
 SHAPES = [
     # T, H, V, S_c, tau, entropy
-    (300, 512, 5000, 4, 1.0, False),   # segments of 1250 = 4 full tiles + 226
-    (77, 256, 2048, 4, 1.0, True),     # segments of exactly 2 tiles
-    (513, 384, 3000, 2, 0.7, True),    # 2 segments of 1500 = 5 tiles + 220, temperature
-    (33, 1024, 1000, 1, 1.0, False),   # one segment, 3 full tiles + 232
-    (1, 128, 4000, 8, 1.0, True),      # a single row, 8 segments of 500
-    (1030, 128, 768, 4, 1.3, True),    # many row tiles, 3 partial tiles of 192
+    (300, 512, 5000, 4, 1.0, False),   # segments of 1250 = 19 full tiles + 34
+    (77, 256, 2048, 4, 1.0, True),     # segments of exactly 8 tiles (2 blocks of 4)
+    (513, 384, 3000, 2, 0.7, True),    # 2 segments of 1500 = 23 tiles + 28, temperature
+    (33, 1024, 1000, 1, 1.0, False),   # one segment, 15 full tiles + 40
+    (1, 128, 4000, 8, 1.0, True),      # a single row, 8 segments of 500 = 7 tiles + 52
+    (1030, 128, 768, 4, 1.3, True),    # many row tiles, segments of 3 tiles (blocks of 4 with one absent)
+    (40, 128, 516, 4, 1.0, True),      # segments of 129 = 2 tiles + a 1-column tile
+    (70, 128, 160, 8, 1.0, False),     # segments of 20 columns: one partial tile each
+    (250, 256, 2500, 1, 1.0, True),    # 40 tiles: two fold groups of 32 and 8
+    (200, 128, 8320, 1, 1.0, False),   # 130 tiles: five fold groups (a tree with a pass-through)
 ]
 
 
@@ -198,6 +202,10 @@ def test_same_row_at_every_tile_position(rlk):
     for bt in (32, 64, 128, 256):
         say(f"replicated row, token_tile={bt}")
         outs.append(lp.forward(dev_bits(h), dev_bits(W), dev_i32(y), token_tile=bt))
+    # the decode-shaped blocks (3 tiles x 64/128/192/256 rows), chosen per launch
+    for sizes in ([60, 90, 150], [256, 44], [1] * 4 + [296]):
+        say(f"replicated row, batches {sizes[:6]}")
+        outs.append(lp.forward(dev_bits(h), dev_bits(W), dev_i32(y), batch_sizes=sizes))
     torch.cuda.synchronize()
     base = host(outs[0]["logp"])
     assert np.all(base.view(np.uint32) == base.view(np.uint32)[0])
