@@ -304,8 +304,8 @@ RLK_API rlk_status_t rlk_logprob_create(const rlk_logprob_config_t* config, int 
   std::memcpy(&epsb, &config->rms_eps, 4);
   char buf[512];
   snprintf(buf, sizeof(buf),
-           "rlk-logprob/v%d;mfma=v_mfma_f32_32x32x16_bf16;kstep=16;bv=%d;H=%d;V=%lld;Sc=%d;"
-           "intile=seq16+pair2+half;segfold=seq%d+pair;segmerge=pair;exp=v_exp_f32(x*0x3fb8aa3b);"
+           "rlk-logprob/v%d;mfma=v_mfma_f32_16x16x32_bf16;kstep=32;bv=%d;H=%d;V=%lld;Sc=%d;"
+           "intile=seq16+pair4;segfold=seq%d+pair;segmerge=pair;exp=v_exp_f32(x*0x3fb8aa3b);"
            "log=v_log_f32*0x3f317218;inv_tau=0x%08x;rms=%d;rms_eps=0x%08x;rsq=v_rsq_f32;"
            "rms_tree=lane-seq8+xor32..1;entropy=%d;contract=off",
            rlk::kContractVersion, rlk::kVocabTile, config->hidden_size,

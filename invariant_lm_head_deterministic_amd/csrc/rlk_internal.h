@@ -8,15 +8,15 @@
 
 namespace rlk {
 
-// ---- numeric contract v2 (every constant here decides result bits) ----
+// ---- numeric contract v3 (every constant here decides result bits) ----
 constexpr int kVocabTile = 64;    // BV: vocab tile width, tiles start at each segment's start
 constexpr int kFoldGroup = 32;    // tiles per sequential group of the segment fold
 constexpr int kMaxFoldGroups = 128;  // groups per segment (segments up to 2^18 columns)
 constexpr int kMaxSegments = 8;   // S_c in {1, 2, 4, 8}
-constexpr int kContractVersion = 2;
+constexpr int kContractVersion = 3;
 
 // ---- launch shapes (free: they never change a result bit) ----
-constexpr int kKStage = 64;       // K elements staged per LDS buffer (4 MFMA steps of 16)
+constexpr int kKStage = 64;       // K elements staged per LDS buffer (2 MFMA steps of 32)
 
 // Arguments of the LM-head tile kernel (one launch = a row range x a range of whole segments).
 struct LmheadArgs {

@@ -1,15 +1,15 @@
 // HIP kernels of the strict-path selected-token logprob, for gfx950 (MI355X) only.
 //
-// Numeric contract v2. Every result bit of a row is decided by the rules below and by nothing
+// Numeric contract v3. Every result bit of a row is decided by the rules below and by nothing
 // else: not by the row's position in a launch, the launch's row count, the token-tile width,
 // the grid, the number of vocab shards, or which CU or XCD ran a block. The pages ask for a
 // forward whose inputs, split, merge order, precisions, rounding points and primitives are all
 // fixed (RL-Kernel v0.1.0 summary page, "Numeric execution contract"; kongchang.com article,
 // "four key links"); these are our choices for each.
 //
-//  C1 logit. z[t,v] is one fp32 accumulator chain of v_mfma_f32_32x32x16_bf16 steps starting at
-//     +0: step i (i = 0 .. H/16-1, ascending) feeds K indices 16i .. 16i+15, lanes 0-31 of the
-//     instruction carrying 16i+0..7 and lanes 32-63 carrying 16i+8..15 for both operands.
+//  C1 logit. z[t,v] is one fp32 accumulator chain of v_mfma_f32_16x16x32_bf16 steps starting at
+//     +0: step i (i = 0 .. H/32-1, ascending) feeds K indices 32i .. 32i+31, lane group g
+//     (lanes 16g .. 16g+15) of the instruction carrying 32i+8g .. 32i+8g+7 for both operands.
 //     No split-K, no atomics (the ROCm fixes list on the RL-Kernel page: a deterministic
 //     MFMA-based GEMM; K-dim reduction and accumulation precision in the boundary table).
 //  C2 temperature. z' = z * inv_temperature in fp32 (skipped when it is 1.0f: x * 1.0f == x).
@@ -17,12 +17,11 @@
 //     tiles of 64 columns from its own start, the last one partial (the "actual vocab range"
 //     and "local reduction" of the "Linear logprob" boundary row).
 //  C4 tile max. m = max of z' over the tile's columns (exact; order-free).
-//  C5 tile sum. e(v) = EXP(z'(v) - m). The tile's 64 columns form 2 blocks of 32 (b = 0, 1)
-//     and two halves h in {0,1}; block b, half h holds the 16 columns
-//     32b + 8(r>>2) + 4h + (r&3), r = 0..15 (the MFMA result-register order). Then
-//        p[b][h] = (((e_r0 + e_r1) + e_r2) + ... ) + e_r15          (sequential in r)
-//        P[h]    = p[0][h] + p[1][h]
-//        s       = P[0] + P[1]
+//  C5 tile sum. e(v) = EXP(z'(v) - m). The tile's 64 columns form 4 blocks of 16 (b = 0..3)
+//     and 4 lane groups g = 0..3; group g holds the 16 columns 16b + 4g + r, b, r = 0..3 (the
+//     MFMA result-register order). Then
+//        p[g] = sequential sum of e over (b, r) = (0,0), (0,1), .., (0,3), (1,0), .., (3,3)
+//        s    = (p[0] + p[1]) + (p[2] + p[3])
 //     Columns past the end of a partial tile contribute exactly +0. (nxbn.cn blog, §3.2 and
 //     §4.3: sequential sums inside a thread, then a fixed tree; fp32 intermediates.)
 //  C6 entropy term (optional). u uses the same tree with terms e(v) * (z'(v) - m).
@@ -61,7 +60,7 @@
 namespace rlk {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 0x1.715476p+0f;  // fl32(log2(e))
@@ -172,66 +171,67 @@ __device__ __forceinline__ bool map_tile(const LmheadArgs& a, Tile& t) {
   return true;
 }
 
-// Fused tile epilogue (C2, C4-C7) on the MFMA result registers of one wave. The wave owns VB
-// column blocks of 32 (block columns 32 VB wv ..), i.e. VB/2 whole tiles, and NTB row blocks of
-// 32 (rows 32 (wt NTB + j) ..), so every reduction of a tile stays inside the wave: lane-local
-// sums plus one exchange between the two lane halves.
-// Target of this lane's row in row block j (-1 past the row tile), read before the K loop so that
-// its latency hides behind the MFMAs.
-template <int NTB>
-__device__ __forceinline__ void load_targets(int (&y)[NTB], const LmheadArgs& a, const Tile& t,
-                                             int wt, int col) {
+// MFMA layout (v_mfma_f32_16x16x32_bf16, vocab = MFMA rows from W, tokens = MFMA columns from
+// the hidden states): an operand fragment is 16 rows x 32 K, lane l holding row l & 15 and the
+// 8 K elements 8 (l >> 4) .. +7; the result block gives lane l the token l & 15 and the 4 vocab
+// rows 4 (l >> 4) + r. A wave owns VB16 vocab blocks and NB16 token blocks of 16.
+
+// Target of this lane's token in token block j (-1 past the row tile), read before the K loop so
+// that its latency hides behind the MFMAs.
+template <int NB16>
+__device__ __forceinline__ void load_targets(int (&y)[NB16], const LmheadArgs& a, const Tile& t,
+                                             int wt, int lane) {
 #pragma unroll
-  for (int j = 0; j < NTB; ++j) {
-    const int rr = 32 * (wt * NTB + j) + col;
+  for (int j = 0; j < NB16; ++j) {
+    const int rr = 16 * (wt * NB16 + j) + (lane & 15);
     y[j] = rr < t.rows ? a.targets[t.row0 + rr] : -1;
   }
 }
 
-template <int VB, int NTB, bool ENT, bool TEMP>
-__device__ __forceinline__ void tile_epilogue(f32x16 (&acc)[VB][NTB], const int (&ytgt)[NTB],
+// Fused tile epilogue (C2, C4-C7) on the MFMA result registers of one wave. The wave owns vocab
+// blocks 16 (VB16 wv + i) .. of the block, i.e. VB16/4 whole tiles, and token blocks
+// 16 (NB16 wt + j) .., so every reduction of a tile stays inside the wave: a lane-local
+// sequential sum plus two exchanges between lane groups.
+template <int VB16, int NB16, bool ENT, bool TEMP>
+__device__ __forceinline__ void tile_epilogue(f32x4 (&acc)[VB16][NB16], const int (&ytgt)[NB16],
                                               const LmheadArgs& a, const Tile& t, int wv, int wt,
-                                              int half, int col) {
-  static_assert(VB % 2 == 0, "a wave owns whole tiles");
+                                              int lane) {
+  static_assert(VB16 % 4 == 0, "a wave owns whole tiles");
+  const int g = lane >> 4;
   if constexpr (TEMP) {
 #pragma unroll
-    for (int i = 0; i < VB; ++i)
+    for (int i = 0; i < VB16; ++i)
 #pragma unroll
-      for (int j = 0; j < NTB; ++j)
+      for (int j = 0; j < NB16; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = acc[i][j][r] * a.inv_tau;
+        for (int r = 0; r < 4; ++r) acc[i][j][r] = acc[i][j][r] * a.inv_tau;
   }
-  // column offset inside a tile of (block b of the tile, register r) for this lane
-  auto coff = [&](int b, int r) { return 32 * b + 8 * (r >> 2) + 4 * half + (r & 3); };
 #pragma unroll
-  for (int c = 0; c < VB / 2; ++c) {
-    const int tc = wv * (VB / 2) + c;  // tile index inside the block
+  for (int c = 0; c < VB16 / 4; ++c) {
+    const int tc = wv * (VB16 / 4) + c;  // tile index inside the block
     const int tlen = min(kVocabTile, t.len - tc * kVocabTile);
     if (tlen <= 0) continue;  // past the segment's end (uniform across the wave)
     const bool partial = tlen < kVocabTile;
     const int64_t go = (int64_t)(t.tile0 + tc - a.g_base) * a.ld;
     const int64_t tstart = t.start + (int64_t)tc * kVocabTile;
 #pragma unroll
-    for (int j = 0; j < NTB; ++j) {
-      const f32x16& z0 = acc[2 * c][j];
-      const f32x16& z1 = acc[2 * c + 1][j];
+    for (int j = 0; j < NB16; ++j) {
       float mm = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (!partial || coff(0, r) < tlen) mm = fmaxf(mm, z0[r]);
-        if (!partial || coff(1, r) < tlen) mm = fmaxf(mm, z1[r]);
-      }
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (!partial || 16 * b + 4 * g + r < tlen) mm = fmaxf(mm, acc[4 * c + b][j][r]);
+      mm = fmaxf(mm, __shfl_xor(mm, 16));
       const float m = fmaxf(mm, __shfl_xor(mm, 32));
-      float p[2], pu[2];
+      float ps = 0.0f, pq = 0.0f;
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const f32x16& z = b ? z1 : z0;
-        float ps = 0.0f, pq = 0.0f;
+      for (int b = 0; b < 4; ++b)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float d = z[r] - m;
+        for (int r = 0; r < 4; ++r) {
+          const float d = acc[4 * c + b][j][r] - m;
           float e = c_exp(d);
-          const bool out = partial && coff(b, r) >= tlen;
+          const bool out = partial && 16 * b + 4 * g + r >= tlen;
           if (out) e = 0.0f;
           ps = ps + e;
           if constexpr (ENT) {
@@ -240,18 +240,16 @@ __device__ __forceinline__ void tile_epilogue(f32x16 (&acc)[VB][NTB], const int 
             pq = pq + q;
           }
         }
-        p[b] = ps;
-        pu[b] = pq;
-      }
-      const float P = p[0] + p[1];
-      const float sum = P + __shfl_xor(P, 32);  // P[0] + P[1] on both halves (commutative)
+      // (p0 + p1) + (p2 + p3) on every lane group (fp32 addition is commutative)
+      const float s1 = ps + __shfl_xor(ps, 16);
+      const float sum = s1 + __shfl_xor(s1, 32);
       float u = 0.0f;
       if constexpr (ENT) {
-        const float PU = pu[0] + pu[1];
-        u = PU + __shfl_xor(PU, 32);
+        const float u1 = pq + __shfl_xor(pq, 16);
+        u = u1 + __shfl_xor(u1, 32);
       }
-      const int rr = 32 * (wt * NTB + j) + col;  // row inside the row tile
-      if (half == 0 && rr < t.rows) {
+      const int rr = 16 * (wt * NB16 + j) + (lane & 15);  // row inside the row tile
+      if (g == 0 && rr < t.rows) {
         const int64_t row = (int64_t)t.row0 + rr;
         a.part_m[go + row] = m;
         a.part_s[go + row] = sum;
@@ -262,15 +260,14 @@ __device__ __forceinline__ void tile_epilogue(f32x16 (&acc)[VB][NTB], const int 
       const int64_t d = (int64_t)y - tstart;
       const bool in_tile = y >= 0 && d >= 0 && d < tlen;
       const int dd = (int)d;
-      const bool mine = in_tile && (((dd >> 2) & 1) == half);
+      const bool mine = in_tile && (((dd >> 2) & 3) == g);
       if (__any(mine)) {
-        const int ridx = (dd >> 5) * 16 + ((dd >> 3) & 3) * 4 + (dd & 3);
+        const int ridx = (dd >> 4) * 4 + (dd & 3);
         float v = 0.0f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          v = (r == ridx) ? z0[r] : v;
-          v = (16 + r == ridx) ? z1[r] : v;
-        }
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v = (4 * b + r == ridx) ? acc[4 * c + b][j][r] : v;
         if (mine) a.tgt[t.row0 + rr] = v;
       }
     }
@@ -278,24 +275,22 @@ __device__ __forceinline__ void tile_epilogue(f32x16 (&acc)[VB][NTB], const int 
 }
 
 // --------------------------------------------------------------------------------------------
-// K1: LM-head tile kernel. One block = one vocab tile (256 columns of one segment) x BT rows.
-// Waves: VW split the tile's 8 column blocks, TW split the rows; each wave owns VB = 8/VW column
-// blocks x NTB row blocks of 32, as 32x32 MFMA result tiles (vocab = MFMA rows, tokens = MFMA
-// columns, so each lane holds one token and 16 vocab columns per block: the per-token vocab
-// reduction is lane-local apart from one half-swap and, for VW > 1, one LDS exchange).
+// K1: LM-head tile kernel. One block = 4 vocab tiles (256 columns of one segment) x BT rows.
+// Waves: VW split the block's columns, TW split the rows; each wave owns VB16 = 16 / VW vocab
+// blocks x NB16 = 2 NTB token blocks of 16 as 16x16 MFMA result tiles (vocab = MFMA rows, tokens
+// = MFMA columns), i.e. whole tiles for its rows, so the epilogue needs no LDS.
 // --------------------------------------------------------------------------------------------
 template <int VW, int TW, int NTB, bool ENT, bool TEMP>
 __global__ void __launch_bounds__(64 * VW * TW)
 k_lmhead(const LmheadArgs a) {
   constexpr int NWAVES = VW * TW;
-  constexpr int NT = 64 * NWAVES;
   constexpr int BT = 32 * NTB * TW;
   constexpr int BW = 4 * kVocabTile;          // block columns: 4 tiles
-  constexpr int VB = BW / 32 / VW;
+  constexpr int VB16 = BW / 16 / VW;          // vocab blocks of 16 per wave
+  constexpr int NB16 = 2 * NTB;               // token blocks of 16 per wave
   constexpr int WI = BW / 8 / NWAVES;          // DMA instructions per wave per W stage
   constexpr int HI = BT / 8 / NWAVES;          // DMA instructions per wave per hidden stage
-  static_assert(VB * VW * 32 == BW && WI * 8 * NWAVES == BW && HI * 8 * NWAVES == BT, "tiling");
-  (void)NT;
+  static_assert(VB16 * VW * 16 == BW && WI * 8 * NWAVES == BW && HI * 8 * NWAVES == BT, "tiling");
 
   // two stages as distinct objects, so the compiler can tell a DMA into one stage from reads
   // of the other and does not wait for the DMA before those reads
@@ -306,25 +301,16 @@ k_lmhead(const LmheadArgs a) {
 
   Tile t;
   if (!map_tile<BT, 4>(a, t)) return;
-  int ytgt[NTB];
-  load_targets<NTB>(ytgt, a, t, (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) / VW,
-                    threadIdx.x & 31);
-  const int64_t tile_start = t.start;
-  const int tile_len = t.len;
-  const int row0 = t.row0;
-  const int H = a.H;
-
-  const uint16_t* __restrict__ Wt = a.W + (tile_start - a.w_row0) * (int64_t)H;
-  const uint16_t* __restrict__ Ht = a.hidden + (int64_t)row0 * H;
-  const int rows_here = t.rows;
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wv = wave % VW;
   const int wt = wave / VW;
-  const int half = lane >> 5;
-  const int col = lane & 31;
+  int ytgt[NB16];
+  load_targets<NB16>(ytgt, a, t, wt, lane);
+  const int H = a.H;
+  const uint16_t* __restrict__ Wt = a.W + (t.start - a.w_row0) * (int64_t)H;
+  const uint16_t* __restrict__ Ht = a.hidden + (int64_t)t.row0 * H;
 
   // Direct-to-LDS staging: DMA instruction q of this wave fills the 8 staged rows starting at
   // 8 (q * NWAVES + wave); lane l writes position l & 7 of row (l >> 3) of that group, so it
@@ -336,16 +322,16 @@ k_lmhead(const LmheadArgs a) {
   for (int q = 0; q < WI; ++q) {
     const int r = 8 * (q * NWAVES + wave) + (lane >> 3);
     const int c = (lane & 7) ^ swz(r);
-    wgo[q] = (uint32_t)(min(r, tile_len - 1) * H + c * 8) * 2u;
+    wgo[q] = (uint32_t)(min(r, t.len - 1) * H + c * 8) * 2u;
   }
 #pragma unroll
   for (int q = 0; q < HI; ++q) {
     const int r = 8 * (q * NWAVES + wave) + (lane >> 3);
     const int c = (lane & 7) ^ swz(r);
-    hgo[q] = (uint32_t)(min(r, rows_here - 1) * H + c * 8) * 2u;
+    hgo[q] = (uint32_t)(min(r, t.rows - 1) * H + c * 8) * 2u;
   }
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(Wt, tile_len * H * 2);
-  const __amdgpu_buffer_rsrc_t rh = make_rsrc(Ht, rows_here * H * 2);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(Wt, t.len * H * 2);
+  const __amdgpu_buffer_rsrc_t rh = make_rsrc(Ht, t.rows * H * 2);
   auto issue = [&](int kc, uint8_t* lw, uint8_t* lh) {
     const uint32_t so = (uint32_t)kc * kRowBytes;
 #pragma unroll
@@ -354,99 +340,97 @@ k_lmhead(const LmheadArgs a) {
     for (int q = 0; q < HI; ++q) dma16(rh, lh + 8 * (q * NWAVES + wave) * kRowBytes, hgo[q], so);
   };
 
-  f32x16 acc[VB][NTB];
+  f32x4 acc[VB16][NB16];
 #pragma unroll
-  for (int i = 0; i < VB; ++i)
+  for (int i = 0; i < VB16; ++i)
 #pragma unroll
-    for (int j = 0; j < NTB; ++j)
+    for (int j = 0; j < NB16; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+      for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0f;
 
-  // Fragment reads: one lane offset per MFMA sub-step (every fragment row has the same
-  // (row >> 1) & 7 as col), the 32-row blocks at constant 4 KB strides.
-  const int sw = swz(col);
-  int loff[4];
+  // Fragment reads: sub-step s (K 32s .. 32s+31 of a stage) reads piece 4s + (lane >> 4) of row
+  // lane & 15 of each 16-row block; every block row has the same (row >> 1) & 7 as lane & 15,
+  // so one lane offset per sub-step serves all blocks, at constant 2 KB strides.
+  const int r16 = lane & 15;
+  int loff[2];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) loff[s] = col * kRowBytes + (((2 * s + half) ^ sw) << 4);
-  const int a0 = 32 * wv * VB * kRowBytes, b0 = 32 * wt * NTB * kRowBytes;
-  bf16x8 fa[2][VB], fb[2][NTB];
-  auto load_frags = [&](const uint8_t* lw, const uint8_t* lh, int s, int buf) {
-    const uint8_t* pa = lw + a0 + loff[s];
-    const uint8_t* pb = lh + b0 + loff[s];
+  for (int s = 0; s < 2; ++s) loff[s] = r16 * kRowBytes + (((4 * s + (lane >> 4)) ^ swz(r16)) << 4);
+  const int a0 = 16 * wv * VB16 * kRowBytes, b0 = 16 * wt * NB16 * kRowBytes;
+  // Register budget (2 waves per SIMD): the W fragments are single-buffered, each re-read right
+  // after the MFMAs of its row block (its next use is (VB16-1) NB16 MFMAs later); the hidden
+  // fragments, used by every row block, are double-buffered.
+  bf16x8 fa[VB16], fb[2][NB16];
+  // One sub-step: MFMAs on fa / fb[cb] while reading the fragments of sub-step ns of the
+  // buffers (lw, lh) into fa / fb[1-cb]; ND DMA instructions spread over the MFMAs.
+  constexpr int NM = VB16 * NB16;  // MFMAs per sub-step
+  auto sub = [&](auto cb_c, auto nd_c, const uint8_t* lw, const uint8_t* lh, int ns) {
+    constexpr int cb = decltype(cb_c)::value;
+    constexpr int ND = decltype(nd_c)::value;
+    const uint8_t* pa = lw + a0 + loff[ns];
+    const uint8_t* pb = lh + b0 + loff[ns];
 #pragma unroll
-    for (int i = 0; i < VB; ++i) fa[buf][i] = *(const bf16x8*)(pa + i * 32 * kRowBytes);
+    for (int j = 0; j < NB16; ++j) fb[1 - cb][j] = *(const bf16x8*)(pb + j * 16 * kRowBytes);
 #pragma unroll
-    for (int j = 0; j < NTB; ++j) fb[buf][j] = *(const bf16x8*)(pb + j * 32 * kRowBytes);
-  };
-  auto mfmas = [&](int buf) {
+    for (int i = 0; i < VB16; ++i) {
 #pragma unroll
-    for (int i = 0; i < VB; ++i)
-#pragma unroll
-      for (int j = 0; j < NTB; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0,
-                                                            0, 0);
-  };
-  // Instruction order inside one sub-step: each MFMA followed by one fragment read for the
-  // next sub-step, DMA instructions spread evenly over the MFMAs.
-  constexpr int NF = VB + NTB;  // fragment reads per sub-step
-  constexpr int NM = VB * NTB;  // MFMAs per sub-step
-  auto sched_sub = [&](auto nreads_c, auto ndma_c) {
-    constexpr int NR = decltype(nreads_c)::value;
-    constexpr int ND = decltype(ndma_c)::value;
+      for (int j = 0; j < NB16; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[cb][j], acc[i][j], 0, 0, 0);
+      fa[i] = *(const bf16x8*)(pa + i * 16 * kRowBytes);
+    }
+    // order: the hidden reads interleaved with the first row block's MFMAs, then one W read
+    // after each row block; DMA instructions every EV MFMAs
     constexpr int NDs = ND > 0 ? ND : 1;
     constexpr int EV = ND > 0 ? (NM / NDs > 0 ? NM / NDs : 1) : NM + 1;
     constexpr int INLOOP = ND > 0 ? (NM / EV < ND ? NM / EV : ND) : 0;
 #pragma unroll
-    for (int i = 0; i < NM; ++i) {
+    for (int n = 0; n < NM; ++n) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (ND > 0 && i % EV == EV - 1 && i / EV < INLOOP)
+      if (n < NB16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (n % NB16 == NB16 - 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (ND > 0 && n % EV == EV - 1 && n / EV < INLOOP)
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
     if constexpr (ND > INLOOP) __builtin_amdgcn_sched_group_barrier(0x020, ND - INLOOP, 0);
+    __builtin_amdgcn_sched_barrier(0);
   };
-  using ICR = std::integral_constant<int, NF>;
-  using IC0 = std::integral_constant<int, 0>;
-  using ICD = std::integral_constant<int, WI + HI>;
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using CD = std::integral_constant<int, WI + HI>;
 
-  // K loop: stages of 64 K, two LDS buffers (distinct objects, so a DMA into one never makes the
-  // compiler wait before reads of the other). Stage k: sub-steps 0-2 run from the fragments in
-  // registers while reading the next sub-step's; then this wave's DMA of stage k+1 is waited
-  // and all waves meet (stage k+1 has landed everywhere, and every read of stage k's buffer is
-  // done); sub-step 3 then issues the DMA of stage k+2 into stage k's buffer and reads the
-  // first fragments of stage k+1. The last two stages issue no DMA and their final fragment
-  // reads are unused (in bounds). H is a multiple of 128, so the stage count is even and the
-  // two buffers alternate statically.
+  // K loop: stages of 64 K (two MFMA sub-steps of 32), two LDS buffers (distinct objects, so a
+  // DMA into one never makes the compiler wait before reads of the other). Stage k: sub-step 0
+  // runs from the fragments in registers while reading sub-step 1's; then this wave's DMA of
+  // stage k+1 is waited and all waves meet (stage k+1 has landed everywhere, and every read of
+  // stage k's buffer is done); sub-step 1 then issues the DMA of stage k+2 into stage k's buffer
+  // and reads the first fragments of stage k+1. The last two stages issue no DMA and their final
+  // fragment reads are unused (in bounds). H is a multiple of 128, so the stage count is even
+  // and the two buffers alternate statically.
   const int nk = H / kKStage;
   auto stage = [&](auto dma, int k, uint8_t* cw, uint8_t* ch, const uint8_t* nw,
                    const uint8_t* nh) {
     constexpr bool D = decltype(dma)::value;
-    mfmas(0);
-    load_frags(cw, ch, 1, 1);
-    sched_sub(ICR{}, IC0{});
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(1);
-    load_frags(cw, ch, 2, 0);
-    sched_sub(ICR{}, IC0{});
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(0);
-    load_frags(cw, ch, 3, 1);
-    sched_sub(ICR{}, IC0{});
-    __builtin_amdgcn_sched_barrier(0);
+    sub(C0{}, C0{}, cw, ch, 1);
     wait_dma();
     __syncthreads();
-    if constexpr (D) issue(k + 2, cw, ch);
-    mfmas(1);
-    load_frags(nw, nh, 0, 0);
-    if constexpr (D) sched_sub(ICR{}, ICD{});
-    else sched_sub(ICR{}, IC0{});
-    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (D) {
+      issue(k + 2, cw, ch);
+      sub(C1{}, CD{}, nw, nh, 0);
+    } else {
+      sub(C1{}, C0{}, nw, nh, 0);
+    }
   };
   issue(0, lds_w0, lds_h0);
   issue(nk > 1 ? 1 : 0, lds_w1, lds_h1);
   __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(WI + HI) : "memory");
   __syncthreads();
-  load_frags(lds_w0, lds_h0, 0, 0);
+  {
+    const uint8_t* pa = lds_w0 + a0 + loff[0];
+    const uint8_t* pb = lds_h0 + b0 + loff[0];
+#pragma unroll
+    for (int j = 0; j < NB16; ++j) fb[0][j] = *(const bf16x8*)(pb + j * 16 * kRowBytes);
+#pragma unroll
+    for (int i = 0; i < VB16; ++i) fa[i] = *(const bf16x8*)(pa + i * 16 * kRowBytes);
+  }
   int k = 0;
   for (; k + 2 < nk; k += 2) {
     stage(std::true_type{}, k, lds_w0, lds_h0, lds_w1, lds_h1);
@@ -456,7 +440,7 @@ k_lmhead(const LmheadArgs a) {
   stage(std::false_type{}, k, lds_w0, lds_h0, lds_w1, lds_h1);
   stage(std::false_type{}, k + 1, lds_w1, lds_h1, lds_w0, lds_h0);
 
-  tile_epilogue<VB, NTB, ENT, TEMP>(acc, ytgt, a, t, wv, wt, half, col);
+  tile_epilogue<VB16, NB16, ENT, TEMP>(acc, ytgt, a, t, wv, wt, lane);
 }
 
 // --------------------------------------------------------------------------------------------
@@ -505,7 +489,8 @@ __global__ void __launch_bounds__(64 * VW * TW) k_lmhead_deep(const LmheadArgs a
   constexpr int NWAVES = VW * TW;
   constexpr int BT = 32 * NTB * TW;
   constexpr int BW = NTPB * kVocabTile;  // block columns
-  constexpr int VB = BW / 32 / VW;
+  constexpr int VB16 = BW / 16 / VW;     // vocab blocks of 16 per wave
+  constexpr int NB16 = 2 * NTB;          // token blocks of 16 per wave
   constexpr int WI = BW / 8 / NWAVES;
   // hidden rows are staged in whole DMA rounds of 8 NWAVES rows; rows past BT repeat the last
   // row and are never read
@@ -513,7 +498,7 @@ __global__ void __launch_bounds__(64 * VW * TW) k_lmhead_deep(const LmheadArgs a
   constexpr int DPS = WI + HI;  // DMA instructions per wave per stage
   constexpr int SW = BW * kRowBytes;
   constexpr int SH = 8 * HI * NWAVES * kRowBytes;
-  static_assert(VB * VW * 32 == BW && VB % 2 == 0 && WI * 8 * NWAVES == BW && BT % 32 == 0,
+  static_assert(VB16 * VW * 16 == BW && VB16 % 4 == 0 && WI * 8 * NWAVES == BW && BT % 32 == 0,
                 "tiling");
   static_assert(NS >= 2 && NS <= 4 && (NS - 2) * DPS <= 63, "stages");
 
@@ -522,19 +507,16 @@ __global__ void __launch_bounds__(64 * VW * TW) k_lmhead_deep(const LmheadArgs a
 
   Tile t;
   if (!map_tile<BT, NTPB>(a, t)) return;
-  int ytgt[NTB];
-  load_targets<NTB>(ytgt, a, t, (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) / VW,
-                    threadIdx.x & 31);
-  const int H = a.H;
-  const uint16_t* __restrict__ Wt = a.W + (t.start - a.w_row0) * (int64_t)H;
-  const uint16_t* __restrict__ Ht = a.hidden + (int64_t)t.row0 * H;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wv = wave % VW;
   const int wt = wave / VW;
-  const int half = lane >> 5;
-  const int col = lane & 31;
+  int ytgt[NB16];
+  load_targets<NB16>(ytgt, a, t, wt, lane);
+  const int H = a.H;
+  const uint16_t* __restrict__ Wt = a.W + (t.start - a.w_row0) * (int64_t)H;
+  const uint16_t* __restrict__ Ht = a.hidden + (int64_t)t.row0 * H;
 
   uint32_t wgo[WI], hgo[HI];
 #pragma unroll
@@ -565,34 +547,36 @@ __global__ void __launch_bounds__(64 * VW * TW) k_lmhead_deep(const LmheadArgs a
       dma16_asm(dh, lh0 + b * SH + 8 * q * NWAVES * kRowBytes, hgo[q], so);
   };
 
-  f32x16 acc[VB][NTB];
+  f32x4 acc[VB16][NB16];
 #pragma unroll
-  for (int i = 0; i < VB; ++i)
+  for (int i = 0; i < VB16; ++i)
 #pragma unroll
-    for (int j = 0; j < NTB; ++j)
+    for (int j = 0; j < NB16; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+      for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0f;
 
-  const int sw = swz(col);
-  int loff[4];
+  // sub-step s (K 32s .. 32s+31 of a stage): piece 4s + (lane >> 4) of row lane & 15 of each
+  // 16-row block (one lane offset per sub-step serves every block, see k_lmhead)
+  const int r16 = lane & 15;
+  int loff[2];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) loff[s] = col * kRowBytes + (((2 * s + half) ^ sw) << 4);
-  const int a0 = 32 * wv * VB * kRowBytes, b0 = 32 * wt * NTB * kRowBytes;
-  bf16x8 fa[2][VB], fb[2][NTB];
+  for (int s = 0; s < 2; ++s) loff[s] = r16 * kRowBytes + (((4 * s + (lane >> 4)) ^ swz(r16)) << 4);
+  const int a0 = 16 * wv * VB16 * kRowBytes, b0 = 16 * wt * NB16 * kRowBytes;
+  bf16x8 fa[2][VB16], fb[2][NB16];
   auto load_frags = [&](int buf, int s, int slot) {
     const uint8_t* pa = lds_w + buf * SW + a0 + loff[s];
     const uint8_t* pb = lds_h + buf * SH + b0 + loff[s];
 #pragma unroll
-    for (int i = 0; i < VB; ++i) fa[slot][i] = *(const bf16x8*)(pa + i * 32 * kRowBytes);
+    for (int j = 0; j < NB16; ++j) fb[slot][j] = *(const bf16x8*)(pb + j * 16 * kRowBytes);
 #pragma unroll
-    for (int j = 0; j < NTB; ++j) fb[slot][j] = *(const bf16x8*)(pb + j * 32 * kRowBytes);
+    for (int i = 0; i < VB16; ++i) fa[slot][i] = *(const bf16x8*)(pa + i * 16 * kRowBytes);
   };
   auto mfmas = [&](int slot) {
 #pragma unroll
-    for (int i = 0; i < VB; ++i)
+    for (int i = 0; i < VB16; ++i)
 #pragma unroll
-      for (int j = 0; j < NTB; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j],
+      for (int j = 0; j < NB16; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[slot][i], fb[slot][j], acc[i][j],
                                                             0, 0, 0);
   };
   // wait until the DMA of stage k+1 is done while up to `later` younger stages stay in flight
@@ -617,10 +601,6 @@ __global__ void __launch_bounds__(64 * VW * TW) k_lmhead_deep(const LmheadArgs a
     const int b = k % NS;
     mfmas(0);
     load_frags(b, 1, 1);
-    mfmas(1);
-    load_frags(b, 2, 0);
-    mfmas(0);
-    load_frags(b, 3, 1);
     // stage k+1 must have landed for every wave; stages k+2 .. k+NS-1 may stay in flight
     const int issued_last = (k - 1 + NS < nk - 1 ? k - 1 + NS : nk - 1);  // newest stage issued
     wait_stage(issued_last - (k + 1));
@@ -631,7 +611,7 @@ __global__ void __launch_bounds__(64 * VW * TW) k_lmhead_deep(const LmheadArgs a
   }
   wait_vm<0>();
 
-  tile_epilogue<VB, NTB, ENT, TEMP>(acc, ytgt, a, t, wv, wt, half, col);
+  tile_epilogue<VB16, NB16, ENT, TEMP>(acc, ytgt, a, t, wv, wt, lane);
 }
 
 // --------------------------------------------------------------------------------------------
