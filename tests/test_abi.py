@@ -128,9 +128,13 @@ def test_longest_segment_is_accepted(lib):
     assert _ws(cfg, l) > 0
 
 
-def test_contract_id_names_the_tile_and_fold(lib):
+def test_fingerprint_names_the_contract_version(lib):
+    # pinned on purpose: a change of the numeric contract must show up here
+    import re
+
     fp = _lib.rlk_build_fingerprint()
-    assert "contract v2" in fp
+    m = re.search(r"contract v(\d+)", fp)
+    assert m and int(m.group(1)) == 3, fp
 
 
 def test_partials_range_must_sit_on_segment_boundaries(lib):
