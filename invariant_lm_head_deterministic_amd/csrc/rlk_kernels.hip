@@ -188,6 +188,60 @@ __device__ __forceinline__ void load_targets(int (&y)[NB16], const LmheadArgs& a
   }
 }
 
+// Reductions across the lane groups of C5 with gfx950's lane-swap instructions (VALU, no LDS):
+// v_permlane16_swap exchanges rows 1 <-> 0 and 3 <-> 2 of 16 lanes between its two operands,
+// v_permlane32_swap the two halves, so with x in both operands every lane gets its own value
+// and its partner's (lane ^ 16, lane ^ 32), always as (even row, odd row) / (low, high): the
+// sum and the max below are the C5 tree ((p0 + p1) + (p2 + p3)) on every lane.
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// One tile (C4-C7) for one token block: z holds this lane's 16 values of the tile (block b,
+// register r at 4 b + r; column 16 b + 4 g + r). MASK: the tile is a segment's partial last
+// tile of tlen columns.
+template <bool MASK, bool ENT>
+__device__ __forceinline__ void tile_one(const float (&z)[16], int g, int tlen, float& m_out,
+                                         float& s_out, float& u_out) {
+  float mm = -INFINITY;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int col = 16 * (q >> 2) + 4 * g + (q & 3);
+    if (!MASK || col < tlen) mm = fmaxf(mm, z[q]);
+  }
+  const float m = max_xor32(max_xor16(mm));
+  float ps = 0.0f, pq = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int col = 16 * (q >> 2) + 4 * g + (q & 3);
+    const float d = z[q] - m;
+    float e = c_exp(d);
+    if (MASK && col >= tlen) e = 0.0f;
+    ps = ps + e;
+    if constexpr (ENT) {
+      float qq = e * d;
+      if (MASK && col >= tlen) qq = 0.0f;
+      pq = pq + qq;
+    }
+  }
+  m_out = m;
+  s_out = sum_xor32(sum_xor16(ps));
+  u_out = ENT ? sum_xor32(sum_xor16(pq)) : 0.0f;
+}
+
 // Fused tile epilogue (C2, C4-C7) on the MFMA result registers of one wave. The wave owns vocab
 // blocks 16 (VB16 wv + i) .. of the block, i.e. VB16/4 whole tiles, and token blocks
 // 16 (NB16 wt + j) .., so every reduction of a tile stays inside the wave: a lane-local
@@ -211,43 +265,16 @@ __device__ __forceinline__ void tile_epilogue(f32x4 (&acc)[VB16][NB16], const in
     const int tc = wv * (VB16 / 4) + c;  // tile index inside the block
     const int tlen = min(kVocabTile, t.len - tc * kVocabTile);
     if (tlen <= 0) continue;  // past the segment's end (uniform across the wave)
-    const bool partial = tlen < kVocabTile;
     const int64_t go = (int64_t)(t.tile0 + tc - a.g_base) * a.ld;
     const int64_t tstart = t.start + (int64_t)tc * kVocabTile;
 #pragma unroll
     for (int j = 0; j < NB16; ++j) {
-      float mm = -INFINITY;
+      float z[16];
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (!partial || 16 * b + 4 * g + r < tlen) mm = fmaxf(mm, acc[4 * c + b][j][r]);
-      mm = fmaxf(mm, __shfl_xor(mm, 16));
-      const float m = fmaxf(mm, __shfl_xor(mm, 32));
-      float ps = 0.0f, pq = 0.0f;
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float d = acc[4 * c + b][j][r] - m;
-          float e = c_exp(d);
-          const bool out = partial && 16 * b + 4 * g + r >= tlen;
-          if (out) e = 0.0f;
-          ps = ps + e;
-          if constexpr (ENT) {
-            float q = e * d;
-            if (out) q = 0.0f;
-            pq = pq + q;
-          }
-        }
-      // (p0 + p1) + (p2 + p3) on every lane group (fp32 addition is commutative)
-      const float s1 = ps + __shfl_xor(ps, 16);
-      const float sum = s1 + __shfl_xor(s1, 32);
-      float u = 0.0f;
-      if constexpr (ENT) {
-        const float u1 = pq + __shfl_xor(pq, 16);
-        u = u1 + __shfl_xor(u1, 32);
-      }
+      for (int q = 0; q < 16; ++q) z[q] = acc[4 * c + (q >> 2)][j][q & 3];
+      float m, sum, u;
+      if (tlen == kVocabTile) tile_one<false, ENT>(z, g, tlen, m, sum, u);
+      else tile_one<true, ENT>(z, g, tlen, m, sum, u);
       const int rr = 16 * (wt * NB16 + j) + (lane & 15);  // row inside the row tile
       if (g == 0 && rr < t.rows) {
         const int64_t row = (int64_t)t.row0 + rr;
@@ -265,9 +292,7 @@ __device__ __forceinline__ void tile_epilogue(f32x4 (&acc)[VB16][NB16], const in
         const int ridx = (dd >> 4) * 4 + (dd & 3);
         float v = 0.0f;
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) v = (4 * b + r == ridx) ? acc[4 * c + b][j][r] : v;
+        for (int q = 0; q < 16; ++q) v = (q == ridx) ? z[q] : v;
         if (mine) a.tgt[t.row0 + rr] = v;
       }
     }
@@ -306,8 +331,6 @@ k_lmhead(const LmheadArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wv = wave % VW;
   const int wt = wave / VW;
-  int ytgt[NB16];
-  load_targets<NB16>(ytgt, a, t, wt, lane);
   const int H = a.H;
   const uint16_t* __restrict__ Wt = a.W + (t.start - a.w_row0) * (int64_t)H;
   const uint16_t* __restrict__ Ht = a.hidden + (int64_t)t.row0 * H;
@@ -440,6 +463,10 @@ k_lmhead(const LmheadArgs a) {
   stage(std::false_type{}, k, lds_w0, lds_h0, lds_w1, lds_h1);
   stage(std::false_type{}, k + 1, lds_w1, lds_h1, lds_w0, lds_h0);
 
+  // the targets of the wave's rows are read only now: held across the K loop they cost the
+  // registers that the loop needs for two waves per SIMD (measured: 4% slower with spills)
+  int ytgt[NB16];
+  load_targets<NB16>(ytgt, a, t, wt, lane);
   tile_epilogue<VB16, NB16, ENT, TEMP>(acc, ytgt, a, t, wv, wt, lane);
 }
 
