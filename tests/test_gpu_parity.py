@@ -63,6 +63,8 @@ SHAPES = [
     (70, 128, 160, 8, 1.0, False),     # segments of 20 columns: one partial tile each
     (250, 256, 2500, 1, 1.0, True),    # 40 tiles: two fold groups of 32 and 8
     (200, 128, 8320, 1, 1.0, False),   # 130 tiles: five fold groups (a tree with a pass-through)
+    (70, 8192, 640, 2, 1.0, True),     # long K loop (128 stages), 5 tiles per segment
+    (20, 65536, 256, 4, 1.0, False),   # the largest hidden size: 1024 stages, 64-column segments
 ]
 
 
