@@ -348,10 +348,43 @@ def torch_native(np, torch, hd, Wd, yd, sizes, ref_logp, steps: int = 5, warmup:
             "_logp": one_h}
 
 
+def long_grpo(rlk, datagen, np, torch, Wd) -> dict:
+    """The long GRPO batch (8 samples x 6912 tokens, 553 trailing pads, the Qwen3-8B head's W): one
+    pass and 8192-row chunks, throughput over the active rows, and the chunked run's bit
+    changes against the one pass."""
+    w = datagen.WORKLOADS["long_grpo"]
+    h = datagen.hidden_bits(w)
+    y = np.load(os.path.join(ROOT, "tests", "golden", "targets_long_grpo.npy"))
+    meta = json.load(open(os.path.join(ROOT, "tests", "golden", "targets_long_grpo.json")))
+    if meta["sha256_hidden"] != datagen.sha256(h):
+        raise RuntimeError("stored long_grpo targets do not belong to the generated inputs")
+    dev = Wd.device
+    hd = torch.from_numpy(h.view(np.int16)).to(dev)
+    yd = torch.from_numpy(y.astype(np.int32)).to(dev)
+    del h
+    lp = rlk.Logprob(w.H, w.V, vocab_segments=w.segments, device=0)
+    active = int((y >= 0).sum())
+    fl = 2.0 * w.T * w.H * w.V
+    one = time_layout(rlk, lp, hd, Wd, yd, None, w.T, 3, 1, {})
+    ch = time_layout(rlk, lp, hd, Wd, yd, None, w.T, 3, 1, dict(row_chunk=8192))
+    out = {"T": w.T, "active_rows": active}
+    for name, r in (("one_pass", one), ("chunks_8192", ch)):
+        out[name] = {"ms_per_step": r["ms_per_step"],
+                     "tokens_per_s": active / (r["ms_per_step"] * 1e-3),
+                     "lmhead_launches": r["lmhead_launches_per_step"],
+                     "lmhead_frac_of_bf16_peak":
+                         fl / (r["lmhead_ms_per_step"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    out["mismatch_count_chunks_vs_one_pass"] = int(np.count_nonzero(
+        one["_logp"].view(np.uint32) != ch["_logp"].view(np.uint32)))
+    del hd, yd, lp
+    return out
+
+
 def extras(rlk, datagen, np, torch, hd, Wd, yd, w, ref_logp) -> dict:
     """The other rows of the path, measured next to the headline: the rollout layout of the TP4
     workload (decode batches x 4 vocab shards; HBM-bound W stream), a plain framework LM head on
-    the same rows, and the fused final RMSNorm + temperature + entropy head."""
+    the same rows, the long GRPO batch in one pass and in chunks, and the fused final RMSNorm +
+    temperature + entropy head."""
     out = {}
     lp = rlk.Logprob(w.H, w.V, vocab_segments=w.segments, device=0)
     sizes = datagen.decode_layout(w.T)
@@ -368,6 +401,8 @@ def extras(rlk, datagen, np, torch, hd, Wd, yd, w, ref_logp) -> dict:
     del lp
     log("extras: torch-native reference path")
     out["torch_native_lm_head"] = torch_native(np, torch, hd, Wd, yd, sizes, ref_logp)
+    log("extras: long_grpo inputs")
+    out["long_grpo"] = long_grpo(rlk, datagen, np, torch, Wd)
     wn = datagen.WORKLOADS["norm_head"]
     log("norm_head inputs")
     x = datagen.hidden_bits(wn)

@@ -139,26 +139,51 @@ struct Tile {
   int rows;       // rows present in the row tile
 };
 
-// Block -> (vocab block, row tile), XCD-aware: consecutive block ids go round-robin to the 8 XCDs,
-// so remap them so that each XCD walks a contiguous range of vocab blocks, a group of 8 vocab
-// blocks at a time across all row tiles (W and hidden tiles shared in L2; 8 was the best of 2,
-// 4, 8, 16 measured on the Qwen3-8B head). Returns false for the few padding blocks.
+// Row tiles per band: the hidden rows of a band stay under ~64 MB, so they stay in the MALL
+// while the band's vocab blocks stream past them.
+template <int BT>
+__host__ __device__ __forceinline__ int64_t band_row_tiles(int H) {
+  const int64_t per = (int64_t)BT * H * 2;
+  const int64_t rb = ((int64_t)64 << 20) / per;
+  return rb > 0 ? rb : 1;
+}
+
+// Blocks of one band of n_tt_band row tiles, rounded up to a multiple of the 8 XCDs.
+__host__ __device__ __forceinline__ int64_t band_blocks(int64_t n_vb, int64_t n_tt_band) {
+  return (n_vb * n_tt_band + 7) / 8 * 8;
+}
+
+// Block -> (vocab block, row tile), XCD-aware. Row tiles go in bands (band_row_tiles), one band
+// after the other in block order; inside a band, consecutive block ids go round-robin to the 8
+// XCDs, so they are remapped so that each XCD walks a contiguous range of the band's items, a
+// group of 8 vocab blocks at a time across the band's row tiles (W and hidden tiles shared in L2;
+// 8 was the best of 2, 4, 8, 16 measured on the Qwen3-8B head). Returns false for the few
+// padding blocks.
 template <int BT, int NTPB>
 __device__ __forceinline__ bool map_tile(const LmheadArgs& a, Tile& t) {
   const int bps = (a.tiles_per_seg + NTPB - 1) / NTPB;  // vocab blocks per segment
   const int n_vb = a.n_seg * bps;
   const int n_tt = (a.rows + BT - 1) / BT;
-  const int64_t n_items = (int64_t)n_vb * n_tt;
-  const int64_t per_xcd = (int64_t)gridDim.x / 8;
-  const int64_t L = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  const int64_t rb = band_row_tiles<BT>(a.H);
+  const int64_t full = band_blocks(n_vb, rb);  // blocks of a full band
+  const int64_t band = (int64_t)blockIdx.x / full;
+  const int64_t bid = (int64_t)blockIdx.x - band * full;
+  const int tt0 = (int)(band * rb);
+  if (tt0 >= n_tt) return false;
+  const int nb_tt = (int)min((int64_t)n_tt - tt0, rb);  // row tiles of this band
+  const int64_t nblk = band_blocks(n_vb, nb_tt);
+  if (bid >= nblk) return false;
+  const int64_t n_items = (int64_t)n_vb * nb_tt;
+  const int64_t per_xcd = nblk / 8;
+  const int64_t L = (bid % 8) * per_xcd + bid / 8;
   if (L >= n_items) return false;
   constexpr int GV = 8;
-  const int64_t grp = L / ((int64_t)GV * n_tt);
+  const int64_t grp = L / ((int64_t)GV * nb_tt);
   const int first_v = (int)(grp * GV);
   const int gsz = min(GV, n_vb - first_v);
-  const int64_t within = L - grp * GV * n_tt;
+  const int64_t within = L - grp * GV * nb_tt;
   const int vb = first_v + (int)(within % gsz);
-  const int tt = (int)(within / gsz);
+  const int tt = tt0 + (int)(within / gsz);
   const int seg = a.seg_begin + vb / bps;
   const int jb = vb % bps;
   const int64_t col0 = (int64_t)jb * NTPB * kVocabTile;
@@ -849,13 +874,16 @@ __global__ void k_clear_status(uint32_t* status) {
 // --------------------------------------------------------------------------------------------
 bool token_tile_supported(int bt) { return bt == 32 || bt == 64 || bt == 128 || bt == 256; }
 
-// Blocks of a launch: vocab blocks of NTPB tiles per segment x row tiles, rounded up to a
-// multiple of 8 (the XCD remap in map_tile; the extra blocks exit at once).
+// Blocks of a launch: per band of row tiles, vocab blocks of NTPB tiles per segment x the band's
+// row tiles, rounded up to a multiple of 8 (the XCD remap in map_tile; extra blocks exit at once).
 template <int BT, int NTPB>
 static int64_t lmhead_blocks(const LmheadArgs& a) {
   const int64_t n_vb = (int64_t)a.n_seg * ((a.tiles_per_seg + NTPB - 1) / NTPB);
   const int64_t n_tt = (a.rows + BT - 1) / BT;
-  return (n_vb * n_tt + 7) / 8 * 8;
+  if (n_vb == 0 || n_tt == 0) return 0;
+  const int64_t rb = band_row_tiles<BT>(a.H);
+  const int64_t n_full = n_tt / rb, rest = n_tt - n_full * rb;
+  return n_full * band_blocks(n_vb, rb) + (rest ? band_blocks(n_vb, rest) : 0);
 }
 
 template <int VW, int TW, int NTB>

@@ -65,6 +65,7 @@ SHAPES = [
     (200, 128, 8320, 1, 1.0, False),   # 130 tiles: five fold groups (a tree with a pass-through)
     (70, 8192, 640, 2, 1.0, True),     # long K loop (128 stages), 5 tiles per segment
     (20, 65536, 256, 4, 1.0, False),   # the largest hidden size: 1024 stages, 64-column segments
+    (600, 65536, 256, 4, 1.0, True),   # 3 row tiles in bands of 2 (hidden rows per band <= 64 MB)
 ]
 
 
