@@ -120,16 +120,37 @@ class Logprob:
         layout, _keep = make_layout(num_rows, **layout_kw)
         return rlk_logprob_workspace_size(self.config, layout)
 
-    def _check(self, t, dtype, name: str):
+    def _check(self, t, dtype, name: str, shape=None):
+        """Device, layout, dtype and shape of a tensor handed to the library: the C ABI takes
+        bare pointers, so a wrong shape here would become an out-of-bounds access there."""
         import torch
 
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
         if t.device.type != "cuda" or t.device.index != self.device:
             raise ValueError(f"{name} must be on cuda:{self.device}")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
         if t.dtype not in dtype:
             raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtype}")
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
         return torch
+
+    def _targets(self, targets):
+        import torch
+
+        self._check(targets, (torch.int32,), "targets")
+        if targets.dim() != 1:
+            raise ValueError("targets must be 1-D [T]")
+        return targets.shape[0]
+
+    def _gamma(self, gamma):
+        import torch
+
+        if gamma is not None:
+            self._check(gamma, (torch.bfloat16, torch.int16, torch.uint16), "gamma",
+                        (self.config.hidden_size,))
 
     def forward(self, hidden, W, targets, *, batch_sizes=None, row_chunk: int = 0,
                 vocab_shards: int = 1, token_tile: int = 0, gamma=None, workspace=None,
@@ -140,26 +161,26 @@ class Logprob:
         import torch
 
         bf = (torch.bfloat16, torch.int16, torch.uint16)
-        self._check(hidden, bf, "hidden")
-        self._check(W, bf, "W")
-        self._check(targets, (torch.int32,), "targets")
-        T = targets.shape[0]
-        if hidden.dim() != 2 or hidden.shape[0] != T or hidden.shape[1] != self.config.hidden_size:
-            raise ValueError("hidden must be [T, H]")
-        if W.dim() != 2 or W.shape[0] != self.config.vocab_size or W.shape[1] != self.config.hidden_size:
-            raise ValueError("W must be [V, H]")
-        if gamma is not None:
-            self._check(gamma, bf, "gamma")
+        H = self.config.hidden_size
+        T = self._targets(targets)
+        self._check(hidden, bf, "hidden", (T, H))
+        self._check(W, bf, "W", (self.config.vocab_size, H))
+        self._gamma(gamma)
         layout, keep = make_layout(T, batch_sizes, row_chunk, vocab_shards, token_tile)
         need = rlk_logprob_workspace_size(self.config, layout)
         dev = torch.device("cuda", self.device)
-        if workspace is None or workspace.numel() * workspace.element_size() < need:
+        if workspace is not None:
+            self._check(workspace, (torch.uint8, torch.int8), "workspace")
+        if workspace is None or workspace.numel() < need:
             workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
         if out is None:
             out = {"logp": torch.empty(T, dtype=torch.float32, device=dev),
                    "lse": torch.empty(T, dtype=torch.float32, device=dev)}
             if self.entropy:
                 out["entropy"] = torch.empty(T, dtype=torch.float32, device=dev)
+        else:
+            for k in ("logp", "lse") + (("entropy",) if self.entropy else ()):
+                self._check(out[k], (torch.float32,), f"out[{k!r}]", (T,))
         s = stream if stream is not None else torch.cuda.current_stream(dev)
         rlk_logprob_forward(self.handle, hidden.data_ptr(), W.data_ptr(), targets.data_ptr(),
                             layout, _ptr(gamma), out["logp"].data_ptr(), out["lse"].data_ptr(),
@@ -172,6 +193,7 @@ class Logprob:
     def device_status(self, workspace, stream=None) -> int:
         import torch
 
+        self._check(workspace, (torch.uint8, torch.int8), "workspace")
         s = stream if stream is not None else torch.cuda.current_stream(
             torch.device("cuda", self.device))
         return rlk_logprob_device_status(self.handle, workspace.data_ptr(), s.cuda_stream)
@@ -181,14 +203,22 @@ class Logprob:
         """One vocab shard's per-segment records, shape [n_local_segments, T, 4] fp32."""
         import torch
 
-        T = targets.shape[0]
+        bf = (torch.bfloat16, torch.int16, torch.uint16)
+        H = self.config.hidden_size
+        T = self._targets(targets)
         dev = torch.device("cuda", self.device)
+        # validates the range (segment boundaries) before any shape is derived from it
         need = rlk_logprob_partials_workspace_size(self.config, T, vocab_begin, vocab_end)
+        self._check(hidden, bf, "hidden", (T, H))
+        self._check(W_shard, bf, "W_shard", (vocab_end - vocab_begin, H))
+        self._gamma(gamma)
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
         seg_len = self.config.vocab_size // self.config.vocab_segments
         nloc = (vocab_end - vocab_begin) // seg_len
         if records is None:
             records = torch.empty((nloc, T, 4), dtype=torch.float32, device=dev)
+        else:
+            self._check(records, (torch.float32,), "records", (nloc, T, 4))
         s = stream if stream is not None else torch.cuda.current_stream(dev)
         rlk_logprob_partials(self.handle, hidden.data_ptr(), W_shard.data_ptr(), vocab_begin,
                              vocab_end, targets.data_ptr(), T, _ptr(gamma), records.data_ptr(),
@@ -199,7 +229,10 @@ class Logprob:
         """Merge the records of all segments ([S_c, T, 4] fp32) into logp, lse[, entropy]."""
         import torch
 
-        T = targets.shape[0]
+        T = self._targets(targets)
+        self._check(records, (torch.float32,), "records", (self.config.vocab_segments, T, 4))
+        if status is not None:
+            self._check(status, (torch.int32, torch.uint32), "status", (1,))
         dev = torch.device("cuda", self.device)
         out = {"logp": torch.empty(T, dtype=torch.float32, device=dev),
                "lse": torch.empty(T, dtype=torch.float32, device=dev)}
