@@ -382,9 +382,9 @@ def long_grpo(rlk, datagen, np, torch, Wd) -> dict:
 
 def extras(rlk, datagen, np, torch, hd, Wd, yd, w, ref_logp) -> dict:
     """The other rows of the path, measured next to the headline: the rollout layout of the TP4
-    workload (decode batches x 4 vocab shards; HBM-bound W stream), a plain framework LM head on
-    the same rows, the long GRPO batch in one pass and in chunks, and the fused final RMSNorm +
-    temperature + entropy head."""
+    workload (decode batches x 4 vocab shards; HBM-bound W stream), the same batch with the
+    portable software EXP/LOG, a plain framework LM head on the same rows, the long GRPO batch in
+    one pass and in chunks, and the fused final RMSNorm + temperature + entropy head."""
     out = {}
     lp = rlk.Logprob(w.H, w.V, vocab_segments=w.segments, device=0)
     sizes = datagen.decode_layout(w.T)
@@ -399,6 +399,17 @@ def extras(rlk, datagen, np, torch, hd, Wd, yd, w, ref_logp) -> dict:
         "mismatch_count_vs_one_pass": int(np.count_nonzero(
             r["_logp"].view(np.uint32) != ref_logp.view(np.uint32)))}
     del lp
+    log("extras: portable primitives")
+    lpp = rlk.Logprob(w.H, w.V, vocab_segments=w.segments, device=0, portable=True)
+    r = time_layout(rlk, lpp, hd, Wd, yd, None, w.T, 5, 2, {})
+    fl = 2.0 * w.T * w.H * w.V
+    out["portable_exp_one_pass"] = {
+        "ms_per_step": r["ms_per_step"], "tokens_per_s": w.T / (r["ms_per_step"] * 1e-3),
+        "lmhead_ms": r["lmhead_ms_per_step"],
+        "lmhead_frac_of_bf16_peak": fl / (r["lmhead_ms_per_step"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "max_abs_diff_logp_vs_default": float(np.max(np.abs(
+            r["_logp"].astype(np.float64) - ref_logp.astype(np.float64))))}
+    del lpp
     log("extras: torch-native reference path")
     out["torch_native_lm_head"] = torch_native(np, torch, hd, Wd, yd, sizes, ref_logp)
     log("extras: long_grpo inputs")

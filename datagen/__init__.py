@@ -213,6 +213,22 @@ def decode_layout(total: int = 4096) -> list[int]:
     return ragged_sizes_cover(total, 1, 256, WORKLOADS["tp4_shards"].cfg)
 
 
+def dyadic_bf16(n_rows: int, n_cols: int, cfg: int, tid: int, k_max: int, log2_den: int,
+                density: float = 1.0) -> np.ndarray:
+    """bf16 bits of k * 2^-log2_den, k uniform on -k_max..k_max (zero where a uniform draw
+    exceeds ``density``). With |k| <= 127 every value is exact in bf16, and products and sums
+    of such values stay on a known dyadic grid, which lets a test reason about exactness.
+    """
+    assert 0 < k_max <= 127
+    g = rng(cfg, tid)
+    k = g.integers(-k_max, k_max + 1, size=(n_rows, n_cols), dtype=np.int8)
+    if density < 1.0:
+        k[g.random(size=(n_rows, n_cols), dtype=np.float32) >= density] = 0
+    table = f32_to_bf16_bits(np.ldexp(np.arange(-k_max, k_max + 1, dtype=np.float64),
+                                      -log2_den).astype(np.float32))
+    return table[k.astype(np.int16) + k_max]
+
+
 def small_case(T: int, H: int, V: int, seed_cfg: int, hidden_scale: float = 1.0,
                w_scale: float = 0.02) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
     """A parity case of arbitrary shape: bf16 hidden, bf16 W, uniform int32 targets.

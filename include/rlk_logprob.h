@@ -72,6 +72,14 @@ typedef enum rlk_status {
 /* rlk_logprob_config_t.flags */
 #define RLK_FLAG_RMSNORM 1u /* apply the final RMSNorm (rms_gamma, rms_eps) to hidden first */
 #define RLK_FLAG_ENTROPY 2u /* also produce the per-row entropy of softmax(z') */
+/* Software EXP, LOG and RSQ built only from IEEE fp32 operations rounded to nearest even (the
+ * "primitives" item of the numeric execution contract on the RL-Kernel v0.1.0 summary page asks
+ * that they be fixed; this fixes them independently of the GPU's transcendental units). With it
+ * every output bit follows from the inputs through operations any IEEE-754 machine performs
+ * identically, so a CPU model of the contract reproduces logp, lse and entropy bit for bit
+ * whenever it reproduces the logits. Costs extra VALU work in the tile epilogue. Part of the
+ * contract id: results differ from the default mode (both stay within 1e-3 of exact). */
+#define RLK_FLAG_PORTABLE_EXP 4u
 
 /* bits of the device status word */
 #define RLK_DEVICE_STATUS_BAD_TARGET 1u

@@ -16,6 +16,7 @@ from . import _lib
 from ._lib import (  # noqa: F401
     RLK_DEVICE_STATUS_BAD_TARGET,
     RLK_FLAG_ENTROPY,
+    RLK_FLAG_PORTABLE_EXP,
     RLK_FLAG_RMSNORM,
     RlkError,
     rlk_build_fingerprint,
@@ -51,14 +52,15 @@ def inv_temperature(tau: float) -> float:
 
 def make_config(hidden_size: int, vocab_size: int, vocab_segments: int = 4,
                 temperature: float = 1.0, rmsnorm: bool = False, rms_eps: float = 1e-6,
-                entropy: bool = False) -> rlk_logprob_config_t:
+                entropy: bool = False, portable: bool = False) -> rlk_logprob_config_t:
     c = rlk_logprob_config_t()
     c.hidden_size = hidden_size
     c.vocab_segments = vocab_segments
     c.vocab_size = vocab_size
     c.inv_temperature = inv_temperature(temperature)
     c.rms_eps = rms_eps if rmsnorm else 0.0
-    c.flags = (RLK_FLAG_RMSNORM if rmsnorm else 0) | (RLK_FLAG_ENTROPY if entropy else 0)
+    c.flags = ((RLK_FLAG_RMSNORM if rmsnorm else 0) | (RLK_FLAG_ENTROPY if entropy else 0)
+               | (RLK_FLAG_PORTABLE_EXP if portable else 0))
     c.reserved = 0
     return c
 
@@ -95,9 +97,9 @@ class Logprob:
 
     def __init__(self, hidden_size: int, vocab_size: int, vocab_segments: int = 4,
                  temperature: float = 1.0, rmsnorm: bool = False, rms_eps: float = 1e-6,
-                 entropy: bool = False, device: int = 0):
+                 entropy: bool = False, device: int = 0, portable: bool = False):
         self.config = make_config(hidden_size, vocab_size, vocab_segments, temperature, rmsnorm,
-                                  rms_eps, entropy)
+                                  rms_eps, entropy, portable)
         self.device = device
         self.entropy = entropy
         self.rmsnorm = rmsnorm

@@ -26,6 +26,7 @@ RLK_ERR_HIP = 8
 
 RLK_FLAG_RMSNORM = 1
 RLK_FLAG_ENTROPY = 2
+RLK_FLAG_PORTABLE_EXP = 4
 RLK_DEVICE_STATUS_BAD_TARGET = 1
 
 

@@ -1,7 +1,8 @@
 """Build the gfx950 HIP library ``librlk_logprob.so`` in-tree with hipcc.
 
 The numeric contract depends on these flags: -ffp-contract=off (no fused multiply-add is formed
-from separate operations), -fno-fast-math, denormals kept, and no packed-fp32 instructions.
+from separate operations), -fno-fast-math, denormals kept, fp32 division and square root correctly rounded, and no
+packed-fp32 instructions.
 """
 
 from __future__ import annotations
@@ -24,6 +25,7 @@ CONTRACT_FLAGS = [
     "-ffp-contract=off",
     "-fno-fast-math",
     "-fno-gpu-flush-denormals-to-zero",
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 

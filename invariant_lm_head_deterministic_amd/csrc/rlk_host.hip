@@ -72,7 +72,7 @@ Geometry geometry(const rlk_logprob_config_t& c) {
 rlk_status_t check_config(const rlk_logprob_config_t* c) {
   if (!c) return fail(RLK_ERR_INVALID_ARGUMENT, "config is NULL");
   if (c->reserved != 0) return fail(RLK_ERR_INVALID_ARGUMENT, "config.reserved must be 0");
-  if (c->flags & ~(RLK_FLAG_RMSNORM | RLK_FLAG_ENTROPY))
+  if (c->flags & ~(RLK_FLAG_RMSNORM | RLK_FLAG_ENTROPY | RLK_FLAG_PORTABLE_EXP))
     return fail(RLK_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", c->flags);
   if (c->hidden_size <= 0 || c->hidden_size % 128 != 0 || c->hidden_size > 65536)
     return fail(RLK_ERR_UNSUPPORTED_SHAPE, "hidden_size %d is not a positive multiple of 128 <= 65536",
@@ -219,6 +219,7 @@ rlk_status_t run_rows(const rlk_logprob* h, const Geometry& g, const void* hidde
       ra.H = c.hidden_size;
       ra.inv_H = 1.0f / (float)c.hidden_size;
       ra.eps = c.rms_eps;
+      ra.portable = (c.flags & RLK_FLAG_PORTABLE_EXP) ? 1 : 0;
       hipError_t e = rlk::launch_rmsnorm(ra, st);
       if (e != hipSuccess) return hip_fail(e, "rmsnorm launch");
     }
@@ -243,6 +244,7 @@ rlk_status_t run_rows(const rlk_logprob* h, const Geometry& g, const void* hidde
   a.n_seg = s1 - s0;
   a.g_base = g_base;
   a.n_cu = h->n_cu;
+  a.portable = (c.flags & RLK_FLAG_PORTABLE_EXP) ? 1 : 0;
   a.inv_tau = c.inv_temperature;
   hipError_t e = rlk::launch_lmhead(a, token_tile, ent, st);
   if (e != hipSuccess) return hip_fail(e, "lm-head launch");
@@ -302,16 +304,19 @@ RLK_API rlk_status_t rlk_logprob_create(const rlk_logprob_config_t* config, int 
   std::memcpy(&itb, &config->inv_temperature, 4);
   uint32_t epsb;
   std::memcpy(&epsb, &config->rms_eps, 4);
-  char buf[512];
+  const bool port = config->flags & RLK_FLAG_PORTABLE_EXP;
+  char buf[640];
   snprintf(buf, sizeof(buf),
            "rlk-logprob/v%d;mfma=v_mfma_f32_16x16x32_bf16;kstep=32;bv=%d;H=%d;V=%lld;Sc=%d;"
-           "intile=seq16+pair4;segfold=seq%d+pair;segmerge=pair;exp=v_exp_f32(x*0x3fb8aa3b);"
-           "log=v_log_f32*0x3f317218;inv_tau=0x%08x;rms=%d;rms_eps=0x%08x;rsq=v_rsq_f32;"
-           "rms_tree=lane-seq8+xor32..1;entropy=%d;contract=off",
+           "intile=seq16+pair4;segfold=seq%d+pair;segmerge=pair;%s;inv_tau=0x%08x;rms=%d;"
+           "rms_eps=0x%08x;%s;rms_tree=lane-seq8+xor32..1;entropy=%d;contract=off",
            rlk::kContractVersion, rlk::kVocabTile, config->hidden_size,
-           (long long)config->vocab_size, config->vocab_segments, rlk::kFoldGroup, itb,
-           (config->flags & RLK_FLAG_RMSNORM) ? 1 : 0,
+           (long long)config->vocab_size, config->vocab_segments, rlk::kFoldGroup,
+           port ? "exp=soft(cw2+taylor7+scale2^n);log=soft(atanh11+cw2)"
+                : "exp=v_exp_f32(x*0x3fb8aa3b);log=v_log_f32*0x3f317218",
+           itb, (config->flags & RLK_FLAG_RMSNORM) ? 1 : 0,
            (config->flags & RLK_FLAG_RMSNORM) ? epsb : 0u,
+           port ? "rsq=1/sqrt(rn)" : "rsq=v_rsq_f32",
            (config->flags & RLK_FLAG_ENTROPY) ? 1 : 0);
   h->contract = buf;
   *out = h;
@@ -431,6 +436,7 @@ rlk_status_t forward_impl(rlk_logprob_t h, const void* hidden, const void* W_lm,
     f.seg_begin = 0;
     f.n_seg = c.vocab_segments;
     f.g_base = 0;
+    f.portable = (c.flags & RLK_FLAG_PORTABLE_EXP) ? 1 : 0;
     e = rlk::launch_fold(f, ent, s);
     if (e != hipSuccess) return hip_fail(e, "segment fold launch");
     rlk::MergeArgs mg;
@@ -445,6 +451,7 @@ rlk_status_t forward_impl(rlk_logprob_t h, const void* hidden, const void* W_lm,
     mg.vocab = c.vocab_size;
     mg.rows = (int32_t)n;
     mg.n_seg = c.vocab_segments;
+    mg.portable = (c.flags & RLK_FLAG_PORTABLE_EXP) ? 1 : 0;
     e = rlk::launch_merge(mg, ent, s);
     if (e != hipSuccess) return hip_fail(e, "merge launch");
   }
@@ -546,6 +553,7 @@ RLK_API rlk_status_t rlk_logprob_partials(rlk_logprob_t h, const void* hidden,
   f.seg_begin = s0;
   f.n_seg = s1 - s0;
   f.g_base = g_base;
+  f.portable = (c.flags & RLK_FLAG_PORTABLE_EXP) ? 1 : 0;
   hipError_t e = rlk::launch_fold(f, ent, s);
   if (e != hipSuccess) return hip_fail(e, "segment fold launch");
   return ok();
@@ -583,6 +591,7 @@ RLK_API rlk_status_t rlk_logprob_merge(rlk_logprob_t h, const rlk_segment_record
   mg.vocab = c.vocab_size;
   mg.rows = (int32_t)num_rows;
   mg.n_seg = c.vocab_segments;
+  mg.portable = (c.flags & RLK_FLAG_PORTABLE_EXP) ? 1 : 0;
   hipError_t e = rlk::launch_merge(mg, ent, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "merge launch");
   return ok();

@@ -37,6 +37,7 @@ struct LmheadArgs {
   int32_t n_seg;            // segments in this launch
   int32_t g_base;           // global tile index stored at partial-array row 0
   int32_t n_cu;             // compute units of the device (picks a launch shape only)
+  int32_t portable;         // RLK_FLAG_PORTABLE_EXP: software EXP/LOG (C11p)
   float inv_tau;
 };
 // A block of the LM-head kernels covers a run of consecutive tiles of one segment (4 tiles,
@@ -58,6 +59,7 @@ struct FoldArgs {
   int32_t seg_begin;
   int32_t n_seg;
   int32_t g_base;
+  int32_t portable;
 };
 
 struct MergeArgs {
@@ -72,6 +74,7 @@ struct MergeArgs {
   int64_t vocab;
   int32_t rows;
   int32_t n_seg;
+  int32_t portable;
 };
 
 struct RmsArgs {
@@ -82,6 +85,7 @@ struct RmsArgs {
   int32_t H;
   float inv_H;              // fl32(1/H)
   float eps;
+  int32_t portable;         // RSQ as a correctly rounded 1/sqrt (C11p)
 };
 
 // Token-tile widths the LM-head kernel can be forced to (0 = chosen per launch).

@@ -43,6 +43,10 @@
 //     RSQ(x) = v_rsq_f32(x). Every other operation is one IEEE fp32 operation, rounded to
 //     nearest even; the library is built with -ffp-contract=off so nothing is fused (nxbn.cn
 //     blog, §3.4 and §4.3).
+//  C11p portable primitives (RLK_FLAG_PORTABLE_EXP): EXP, LOG and RSQ are p_exp, p_log and
+//     p_rsq below, made of IEEE fp32 operations only, so C1-C12 then fix every output bit as a
+//     function of the logits on any IEEE-754 machine, not only on this GPU's transcendental
+//     units.
 //  C12 RMSNorm (optional). ss = sum of x_k^2 in fp32 — lane l of a 64-wide wave takes the
 //     8-element groups l, l+64, l+128, ... in order, sequentially — then a butterfly over lanes
 //     with xor distances 32, 16, 8, 4, 2, 1; r = RSQ(ss * fl32(1/H) + eps);
@@ -70,6 +74,89 @@ constexpr int kRowBytes = kKStage * 2;    // bytes of one staged row (128)
 __device__ __forceinline__ float c_exp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 __device__ __forceinline__ float c_log(float x) { return __builtin_amdgcn_logf(x) * kLn2; }
 __device__ __forceinline__ float c_rsq(float x) { return __builtin_amdgcn_rsqf(x); }
+
+// Portable EXP and LOG (RLK_FLAG_PORTABLE_EXP, C11p): every step is one IEEE fp32 operation
+// rounded to nearest even, a round-to-integral-even, or an exact integer or bit operation, so
+// any IEEE machine that runs the same steps gets the same bits.
+//  EXP: x = n ln2 + r by Cody and Waite's reduction, ln2 = C1 + C2 with C1 = 0.693359375 (9
+//  significant bits, so n C1 is exact); e^r by its Taylor polynomial to r^7/7! in Horner form
+//  (|r| <= 0.347: truncation below 6e-9 relative); then the scaling by 2^n, built from exponent
+//  bits, in two steps near overflow and below 2^-126 so that every result rounds once.
+//  LOG: x = (1 + f) 2^k with 1 + f in [sqrt(1/2), sqrt(2)]; s = f / (2 + f) and
+//  log(1 + f) = 2 atanh(s) by its odd series to s^11/11 (|s| <= 0.172: truncation below 6e-11),
+//  arranged around the exact f; then k C1 + (that + k C2). RSQ is 1 / sqrt(x), both correctly
+//  rounded. Measured against float64: EXP within 1.2 ulp, LOG 0.83 ulp, RSQ 1.5 ulp.
+constexpr float kLn2C1 = 0x1.63p-1f;        // 0.693359375
+constexpr float kLn2C2 = -0x1.bd0106p-13f;  // fl32(ln2 - C1)
+
+__device__ __forceinline__ float pow2i(int n) { return __int_as_float((n + 127) << 23); }
+
+__device__ __forceinline__ float p_exp(float x) {
+  // Branch-free: out-of-range inputs are clamped for the arithmetic and their result replaced.
+  const float xc = fminf(fmaxf(x, -0x1.9fe368p+6f), 0x1.62e430p+6f);
+  const float nf = __builtin_rintf(xc * kLog2e);
+  const int n = (int)nf;  // -150 .. 128
+  const float r = (xc - nf * kLn2C1) - nf * kLn2C2;
+  float p = 0x1.a01a02p-13f;    // 1/7!
+  p = p * r + 0x1.6c16c2p-10f;  // 1/6!
+  p = p * r + 0x1.111112p-7f;   // 1/5!
+  p = p * r + 0x1.555556p-5f;   // 1/4!
+  p = p * r + 0x1.555556p-3f;   // 1/3!
+  p = p * r + 0.5f;
+  p = p * r + 1.0f;
+  p = p * r + 1.0f;
+  // 2^n as 2^(n - n2) 2^n2 with both factors normal: the first product is exact, the second
+  // rounds once (n2 = 0 in the normal range, -64 below 2^-126, +1 at n = 128).
+  const int n2 = n < -126 ? -64 : (n > 127 ? 1 : 0);
+  float y = (p * pow2i(n - n2)) * pow2i(n2);
+  y = x < -0x1.9fe368p+6f ? 0.0f : y;        // below fl32(ln(2^-150)): rounds to +0
+  y = x > 0x1.62e430p+6f ? INFINITY : y;     // above fl32(ln(FLT_MAX)): overflows
+  return x != x ? x : y;
+}
+
+__device__ __forceinline__ float p_log(float x) {
+  if (x != x || x < 0.0f) return __builtin_nanf("");
+  if (x == 0.0f) return -INFINITY;
+  if (x == INFINITY) return x;
+  int adj = 0;
+  if (x < 0x1p-126f) {
+    x = x * 0x1p23f;  // exact: subnormal -> normal
+    adj = -23;
+  }
+  const uint32_t u = __float_as_uint(x);
+  int k = (int)((u >> 23) & 0xffu) - 127 + adj;
+  float m = __uint_as_float((u & 0x007fffffu) | 0x3f800000u);  // [1, 2)
+  if (m > 0x1.6a09e6p+0f) {  // fl32(sqrt(2))
+    m = m * 0.5f;
+    k = k + 1;
+  }
+  const float f = m - 1.0f;
+  const float s = f / (f + 2.0f);
+  const float z = s * s;
+  float R = 0x1.745d18p-3f;    // 2/11
+  R = R * z + 0x1.c71c72p-3f;  // 2/9
+  R = R * z + 0x1.24924ap-2f;  // 2/7
+  R = R * z + 0x1.99999ap-2f;  // 2/5
+  R = R * z + 0x1.555556p-1f;  // 2/3
+  R = R * z;
+  const float hfsq = 0.5f * (f * f);
+  const float kf = (float)k;
+  // log(1 + f) = 2s + s R = f - (f^2/2 - s (f^2/2 + R)): the exact f carries the leading bits
+  return kf * kLn2C1 + (f - (hfsq - (s * (hfsq + R) + kf * kLn2C2)));
+}
+
+__device__ __forceinline__ float p_rsq(float x) { return 1.0f / __builtin_sqrtf(x); }
+
+template <bool PORT>
+__device__ __forceinline__ float EXP(float x) {
+  if constexpr (PORT) return p_exp(x);
+  else return c_exp(x);
+}
+template <bool PORT>
+__device__ __forceinline__ float LOG(float x) {
+  if constexpr (PORT) return p_log(x);
+  else return c_log(x);
+}
 
 __device__ __forceinline__ uint16_t bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -238,7 +325,7 @@ __device__ __forceinline__ float max_xor32(float x) {
 // One tile (C4-C7) for one token block: z holds this lane's 16 values of the tile (block b,
 // register r at 4 b + r; column 16 b + 4 g + r). MASK: the tile is a segment's partial last
 // tile of tlen columns.
-template <bool MASK, bool ENT>
+template <bool MASK, bool ENT, bool PORT>
 __device__ __forceinline__ void tile_one(const float (&z)[16], int g, int tlen, float& m_out,
                                          float& s_out, float& u_out) {
   float mm = -INFINITY;
@@ -253,7 +340,7 @@ __device__ __forceinline__ void tile_one(const float (&z)[16], int g, int tlen, 
   for (int q = 0; q < 16; ++q) {
     const int col = 16 * (q >> 2) + 4 * g + (q & 3);
     const float d = z[q] - m;
-    float e = c_exp(d);
+    float e = EXP<PORT>(d);
     if (MASK && col >= tlen) e = 0.0f;
     ps = ps + e;
     if constexpr (ENT) {
@@ -271,7 +358,7 @@ __device__ __forceinline__ void tile_one(const float (&z)[16], int g, int tlen, 
 // blocks 16 (VB16 wv + i) .. of the block, i.e. VB16/4 whole tiles, and token blocks
 // 16 (NB16 wt + j) .., so every reduction of a tile stays inside the wave: a lane-local
 // sequential sum plus two exchanges between lane groups.
-template <int VB16, int NB16, bool ENT, bool TEMP>
+template <int VB16, int NB16, bool ENT, bool TEMP, bool PORT>
 __device__ __forceinline__ void tile_epilogue(f32x4 (&acc)[VB16][NB16], const int (&ytgt)[NB16],
                                               const LmheadArgs& a, const Tile& t, int wv, int wt,
                                               int lane) {
@@ -298,8 +385,8 @@ __device__ __forceinline__ void tile_epilogue(f32x4 (&acc)[VB16][NB16], const in
 #pragma unroll
       for (int q = 0; q < 16; ++q) z[q] = acc[4 * c + (q >> 2)][j][q & 3];
       float m, sum, u;
-      if (tlen == kVocabTile) tile_one<false, ENT>(z, g, tlen, m, sum, u);
-      else tile_one<true, ENT>(z, g, tlen, m, sum, u);
+      if (tlen == kVocabTile) tile_one<false, ENT, PORT>(z, g, tlen, m, sum, u);
+      else tile_one<true, ENT, PORT>(z, g, tlen, m, sum, u);
       const int rr = 16 * (wt * NB16 + j) + (lane & 15);  // row inside the row tile
       if (g == 0 && rr < t.rows) {
         const int64_t row = (int64_t)t.row0 + rr;
@@ -330,7 +417,7 @@ __device__ __forceinline__ void tile_epilogue(f32x4 (&acc)[VB16][NB16], const in
 // blocks x NB16 = 2 NTB token blocks of 16 as 16x16 MFMA result tiles (vocab = MFMA rows, tokens
 // = MFMA columns), i.e. whole tiles for its rows, so the epilogue needs no LDS.
 // --------------------------------------------------------------------------------------------
-template <int VW, int TW, int NTB, bool ENT, bool TEMP>
+template <int VW, int TW, int NTB, bool ENT, bool TEMP, bool PORT>
 __global__ void __launch_bounds__(64 * VW * TW)
 k_lmhead(const LmheadArgs a) {
   constexpr int NWAVES = VW * TW;
@@ -492,7 +579,7 @@ k_lmhead(const LmheadArgs a) {
   // registers that the loop needs for two waves per SIMD (measured: 4% slower with spills)
   int ytgt[NB16];
   load_targets<NB16>(ytgt, a, t, wt, lane);
-  tile_epilogue<VB16, NB16, ENT, TEMP>(acc, ytgt, a, t, wv, wt, lane);
+  tile_epilogue<VB16, NB16, ENT, TEMP, PORT>(acc, ytgt, a, t, wv, wt, lane);
 }
 
 // --------------------------------------------------------------------------------------------
@@ -536,7 +623,7 @@ __device__ __forceinline__ void wait_vm() {
   __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(D) : "memory");
 }
 
-template <int VW, int TW, int NTB, int NS, int NTPB, bool ENT, bool TEMP>
+template <int VW, int TW, int NTB, int NS, int NTPB, bool ENT, bool TEMP, bool PORT>
 __global__ void __launch_bounds__(64 * VW * TW) k_lmhead_deep(const LmheadArgs a) {
   constexpr int NWAVES = VW * TW;
   constexpr int BT = 32 * NTB * TW;
@@ -663,7 +750,7 @@ __global__ void __launch_bounds__(64 * VW * TW) k_lmhead_deep(const LmheadArgs a
   }
   wait_vm<0>();
 
-  tile_epilogue<VB16, NB16, ENT, TEMP>(acc, ytgt, a, t, wv, wt, lane);
+  tile_epilogue<VB16, NB16, ENT, TEMP, PORT>(acc, ytgt, a, t, wv, wt, lane);
 }
 
 // --------------------------------------------------------------------------------------------
@@ -674,7 +761,7 @@ __global__ void __launch_bounds__(64 * VW * TW) k_lmhead_deep(const LmheadArgs a
 // --------------------------------------------------------------------------------------------
 constexpr int kFoldWaves = 16;
 
-template <bool ENT>
+template <bool ENT, bool PORT>
 __global__ void __launch_bounds__(64 * kFoldWaves) k_segment_fold(const FoldArgs a) {
   constexpr int G = kFoldGroup;
   constexpr int U = 8;  // loads issued ahead of the arithmetic
@@ -729,7 +816,7 @@ __global__ void __launch_bounds__(64 * kFoldWaves) k_segment_fold(const FoldArgs
       for (int u = 0; u < U; ++u) {
         if (j0 + u < j1) {
           const float dm = vm[u] - M;
-          const float e = c_exp(dm);
+          const float e = EXP<PORT>(dm);
           A = A + vs[u] * e;
           if constexpr (ENT) B = B + (vu[u] + vs[u] * dm) * e;
         }
@@ -762,7 +849,7 @@ __global__ void __launch_bounds__(64 * kFoldWaves) k_segment_fold(const FoldArgs
 // --------------------------------------------------------------------------------------------
 // K2b: per row cross-segment merge and outputs (C9, C10).
 // --------------------------------------------------------------------------------------------
-template <int NS, bool ENT>
+template <int NS, bool ENT, bool PORT>
 __device__ __forceinline__ void merge_row(const MergeArgs& a, int t, int32_t y) {
   float Ms[NS], Ss[NS], Us[NS];
 #pragma unroll
@@ -779,12 +866,12 @@ __device__ __forceinline__ void merge_row(const MergeArgs& a, int t, int32_t y) 
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const float dm = Ms[s] - M;
-    const float e = c_exp(dm);
+    const float e = EXP<PORT>(dm);
     as[s] = Ss[s] * e;
     if constexpr (ENT) au[s] = (Us[s] + Ss[s] * dm) * e;
   }
   const float S = tree_sum<NS>(as);
-  const float logS = c_log(S);
+  const float logS = LOG<PORT>(S);
   const float lse = M + logS;
   const int owner = (int)((int64_t)y / a.seg_len);
   const float zy = a.rec[(int64_t)owner * a.rec_ld + t].tgt;
@@ -796,7 +883,7 @@ __device__ __forceinline__ void merge_row(const MergeArgs& a, int t, int32_t y) 
   }
 }
 
-template <bool ENT>
+template <bool ENT, bool PORT>
 __global__ void __launch_bounds__(256) k_merge(const MergeArgs a) {
   const int t = blockIdx.x * 256 + threadIdx.x;
   if (t >= a.rows) return;
@@ -816,10 +903,10 @@ __global__ void __launch_bounds__(256) k_merge(const MergeArgs a) {
     return;
   }
   switch (a.n_seg) {
-    case 1: merge_row<1, ENT>(a, t, y); break;
-    case 2: merge_row<2, ENT>(a, t, y); break;
-    case 4: merge_row<4, ENT>(a, t, y); break;
-    default: merge_row<8, ENT>(a, t, y); break;
+    case 1: merge_row<1, ENT, PORT>(a, t, y); break;
+    case 2: merge_row<2, ENT, PORT>(a, t, y); break;
+    case 4: merge_row<4, ENT, PORT>(a, t, y); break;
+    default: merge_row<8, ENT, PORT>(a, t, y); break;
   }
 }
 
@@ -850,7 +937,8 @@ __global__ void __launch_bounds__(256) k_rmsnorm(const RmsArgs a) {
   ss = ss + __shfl_xor(ss, 4);
   ss = ss + __shfl_xor(ss, 2);
   ss = ss + __shfl_xor(ss, 1);
-  const float r = c_rsq(ss * a.inv_H + a.eps);
+  const float v = ss * a.inv_H + a.eps;
+  const float r = a.portable ? p_rsq(v) : c_rsq(v);
   for (int p = lane; p < npieces; p += 64) {
     const u32x4 v = *(const u32x4*)(x + p * 8);
     const u32x4 g = *(const u32x4*)(a.gamma + p * 8);
@@ -886,6 +974,22 @@ static int64_t lmhead_blocks(const LmheadArgs& a) {
   return n_full * band_blocks(n_vb, rb) + (rest ? band_blocks(n_vb, rest) : 0);
 }
 
+// Calls f with the entropy, temperature and portable-primitive modes of a launch as compile-time
+// constants, so each kernel instance carries only the epilogue it runs.
+template <class F>
+static void with_modes(const LmheadArgs& a, bool ent, F&& f) {
+  using T = std::true_type;
+  using N = std::false_type;
+  const bool temp = a.inv_tau != 1.0f;
+  if (a.portable) {
+    if (ent) temp ? f(T{}, T{}, T{}) : f(T{}, N{}, T{});
+    else temp ? f(N{}, T{}, T{}) : f(N{}, N{}, T{});
+  } else {
+    if (ent) temp ? f(T{}, T{}, N{}) : f(T{}, N{}, N{});
+    else temp ? f(N{}, T{}, N{}) : f(N{}, N{}, N{});
+  }
+}
+
 template <int VW, int TW, int NTB>
 static hipError_t launch_variant(const LmheadArgs& a, bool ent, hipStream_t s) {
   constexpr int BT = 32 * NTB * TW;
@@ -893,14 +997,9 @@ static hipError_t launch_variant(const LmheadArgs& a, bool ent, hipStream_t s) {
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)blocks), block(64 * VW * TW);
-  const bool temp = a.inv_tau != 1.0f;
-  if (ent) {
-    if (temp) hipLaunchKernelGGL((k_lmhead<VW, TW, NTB, true, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_lmhead<VW, TW, NTB, true, false>), grid, block, 0, s, a);
-  } else {
-    if (temp) hipLaunchKernelGGL((k_lmhead<VW, TW, NTB, false, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_lmhead<VW, TW, NTB, false, false>), grid, block, 0, s, a);
-  }
+  with_modes(a, ent, [&](auto e, auto t, auto p) {
+    hipLaunchKernelGGL((k_lmhead<VW, TW, NTB, e.value, t.value, p.value>), grid, block, 0, s, a);
+  });
   return hipGetLastError();
 }
 
@@ -911,14 +1010,10 @@ static hipError_t launch_deep(const LmheadArgs& a, bool ent, hipStream_t s) {
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)blocks), block(64 * VW * TW);
-  const bool temp = a.inv_tau != 1.0f;
-  if (ent) {
-    if (temp) hipLaunchKernelGGL((k_lmhead_deep<VW, TW, NTB, NS, NTPB, true, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_lmhead_deep<VW, TW, NTB, NS, NTPB, true, false>), grid, block, 0, s, a);
-  } else {
-    if (temp) hipLaunchKernelGGL((k_lmhead_deep<VW, TW, NTB, NS, NTPB, false, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_lmhead_deep<VW, TW, NTB, NS, NTPB, false, false>), grid, block, 0, s, a);
-  }
+  with_modes(a, ent, [&](auto e, auto t, auto p) {
+    hipLaunchKernelGGL((k_lmhead_deep<VW, TW, NTB, NS, NTPB, e.value, t.value, p.value>), grid,
+                       block, 0, s, a);
+  });
   return hipGetLastError();
 }
 
@@ -960,16 +1055,26 @@ hipError_t launch_fold(const FoldArgs& a, bool ent, hipStream_t s) {
   if (a.rows == 0 || a.n_seg == 0) return hipSuccess;
   if ((a.tiles_per_seg + kFoldGroup - 1) / kFoldGroup > kMaxFoldGroups) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((a.rows + 63) / 64), (unsigned)a.n_seg), block(64 * kFoldWaves);
-  if (ent) hipLaunchKernelGGL(k_segment_fold<true>, grid, block, 0, s, a);
-  else hipLaunchKernelGGL(k_segment_fold<false>, grid, block, 0, s, a);
+  if (a.portable) {
+    if (ent) hipLaunchKernelGGL((k_segment_fold<true, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_segment_fold<false, true>), grid, block, 0, s, a);
+  } else {
+    if (ent) hipLaunchKernelGGL((k_segment_fold<true, false>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_segment_fold<false, false>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_merge(const MergeArgs& a, bool ent, hipStream_t s) {
   if (a.rows == 0) return hipSuccess;
   const dim3 grid((unsigned)((a.rows + 255) / 256)), block(256);
-  if (ent) hipLaunchKernelGGL(k_merge<true>, grid, block, 0, s, a);
-  else hipLaunchKernelGGL(k_merge<false>, grid, block, 0, s, a);
+  if (a.portable) {
+    if (ent) hipLaunchKernelGGL((k_merge<true, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_merge<false, true>), grid, block, 0, s, a);
+  } else {
+    if (ent) hipLaunchKernelGGL((k_merge<true, false>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_merge<false, false>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -143,3 +143,18 @@ def test_partials_range_must_sit_on_segment_boundaries(lib):
     with pytest.raises(_lib.RlkError) as e:
         _lib.rlk_logprob_partials_workspace_size(cfg, 128, 100, 37984)
     assert e.value.status == _lib.RLK_ERR_CONTRACT
+
+
+def test_flag_bits(lib):
+    l, _k = make_layout(8)
+    base = _ws(make_config(256, 1000, entropy=True), l)
+    port = make_config(256, 1000, entropy=True, rmsnorm=True, portable=True)
+    assert port.flags == (_lib.RLK_FLAG_ENTROPY | _lib.RLK_FLAG_RMSNORM
+                          | _lib.RLK_FLAG_PORTABLE_EXP)
+    assert _ws(make_config(256, 1000, entropy=True, portable=True), l) == base
+    assert _ws(port, l) >= base
+    bad = make_config(256, 1000)
+    bad.flags = 8
+    with pytest.raises(_lib.RlkError) as e:
+        _ws(bad, l)
+    assert e.value.status == _lib.RLK_ERR_INVALID_ARGUMENT
