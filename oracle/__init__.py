@@ -14,6 +14,8 @@ computes the unsplit reduction. Parity status of each function is stated in its 
 ``oracle.logprob.PINS``.
 """
 
+from .backward import dlogits, grads  # noqa: F401
+from .backward import PINS as BACKWARD_PINS  # noqa: F401
 from .logprob import (  # noqa: F401
     PINS,
     bf16_bits_to_f64,
