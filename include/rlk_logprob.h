@@ -184,6 +184,48 @@ rlk_status_t rlk_logprob_device_status(rlk_logprob_t handle, const void* workspa
  * bitwise-identical rows exactly when their contract ids are equal. */
 const char* rlk_logprob_contract_id(rlk_logprob_t handle);
 
+/* ---- Backward ----------------------------------------------------------------------------
+ * Gradients of L = sum_t grad_logp[t] logp[t] + sum_t grad_entropy[t] entropy[t] (the forward's
+ * outputs) with respect to the LM-head input and W_lm. The training side differentiates the
+ * recomputed logprob, so the library that fixes the forward provides its backward with fixed
+ * numerics too (nxbn.cn blog, §3.3 on the training-side integration; §4.2, an autograd wrapper
+ * routing log_softmax's backward to the same library). Contract B1-B3:
+ *  B1 dz[t, v] = bf16( (g_t (delta(v = y_t) - p) - gH_t p (z' - lse_t + entropy_t)) inv_tau ),
+ *     p = EXP(z' - lse_t), z' recomputed bit for bit as in the forward, in fp32 as written;
+ *     rows with y_t < 0 give 0.
+ *  B2 grad_hidden = pairwise tree over the vocab segments (in order) of one fp32 MFMA chain per
+ *     segment over its vocab indices ascending: bitwise independent of row chunking and equal to
+ *     a vocab-sharded computation that merges per-segment partials in that tree.
+ *  B3 grad_W = one fp32 MFMA chain over rows ascending (32 at a time, rows padded with zeros to a
+ *     multiple of 128), from 0 or, with RLK_BWD_ACCUMULATE, continuing from grad_W's contents;
+ *     any row_chunk (a multiple of 128) therefore gives the bits of one pass.
+ * The final RMSNorm's backward is not built: a handle with RLK_FLAG_RMSNORM is refused. */
+#define RLK_BWD_ACCUMULATE 1u /* grad_W continues the chain from its current contents */
+
+/* Workspace bytes for rlk_logprob_backward with both gradients requested (an upper bound for
+ * fewer). row_chunk: 0 (all rows at once) or a positive multiple of 128. About
+ * 2 V_pad (H + 2 rows_per_chunk) + 4 S_c rows_per_chunk H bytes (V_pad = V rounded up per
+ * segment to 128). */
+rlk_status_t rlk_logprob_backward_workspace_size(const rlk_logprob_config_t* config,
+                                                 int64_t num_rows, int64_t row_chunk,
+                                                 size_t* bytes);
+
+/* hidden bf16 [T, H], W_lm bf16 [V, H], targets int32 [T] (negative = padded): the forward's
+ * inputs. lse fp32 [T] and (with grad_entropy) entropy fp32 [T]: the forward's outputs for these
+ * rows under this handle. grad_logp fp32 [T]; grad_entropy fp32 [T] or NULL (needs
+ * RLK_FLAG_ENTROPY). Outputs (each optional, at least one): grad_hidden fp32 [T, H],
+ * grad_W fp32 [V, H]; rms_gamma and grad_gamma must be NULL. flags: RLK_BWD_ACCUMULATE or 0.
+ * All device pointers 16-byte aligned; the workspace (device, caller-owned) at least
+ * rlk_logprob_backward_workspace_size() bytes. Enqueues on stream without synchronizing or
+ * allocating. Errors are returned before anything is enqueued. */
+rlk_status_t rlk_logprob_backward(rlk_logprob_t handle, const void* hidden, const void* W_lm,
+                                  const int32_t* targets, int64_t num_rows,
+                                  const void* rms_gamma, const float* lse, const float* entropy,
+                                  const float* grad_logp, const float* grad_entropy,
+                                  float* grad_hidden, float* grad_W, float* grad_gamma,
+                                  uint32_t flags, int64_t row_chunk, void* workspace,
+                                  size_t workspace_bytes, rlk_stream_t stream);
+
 /* Compiler, flags and target the library was built with. */
 const char* rlk_build_fingerprint(void);
 

@@ -14,6 +14,7 @@ import numpy as np
 
 from . import _lib
 from ._lib import (  # noqa: F401
+    RLK_BWD_ACCUMULATE,
     RLK_DEVICE_STATUS_BAD_TARGET,
     RLK_FLAG_ENTROPY,
     RLK_FLAG_PORTABLE_EXP,
@@ -23,6 +24,8 @@ from ._lib import (  # noqa: F401
     rlk_layout_check,
     rlk_logprob_config_t,
     rlk_logprob_contract_id,
+    rlk_logprob_backward,
+    rlk_logprob_backward_workspace_size,
     rlk_logprob_create,
     rlk_logprob_destroy,
     rlk_logprob_device_status,
@@ -226,6 +229,57 @@ class Logprob:
                              vocab_end, targets.data_ptr(), T, _ptr(gamma), records.data_ptr(),
                              ws.data_ptr(), ws.numel(), s.cuda_stream)
         return records
+
+    def backward(self, hidden, W, targets, lse, grad_logp, *, entropy=None, grad_entropy=None,
+                 want_hidden: bool = True, want_W: bool = True, grad_W=None,
+                 accumulate: bool = False, row_chunk: int = 0, workspace=None,
+                 stream=None) -> dict:
+        """Gradients of sum_t grad_logp[t] logp[t] (+ grad_entropy[t] entropy[t]) with respect
+        to the LM-head input ("grad_hidden", fp32 [T, H]) and W ("grad_W", fp32 [V, H]).
+        lse (and entropy) are the forward's outputs for these rows. grad_W may be given (fp32
+        [V, H]) to write into; with accumulate=True the chain continues from its contents."""
+        import torch
+
+        bf = (torch.bfloat16, torch.int16, torch.uint16)
+        H = self.config.hidden_size
+        V = self.config.vocab_size
+        T = self._targets(targets)
+        self._check(hidden, bf, "hidden", (T, H))
+        self._check(W, bf, "W", (V, H))
+        self._check(lse, (torch.float32,), "lse", (T,))
+        self._check(grad_logp, (torch.float32,), "grad_logp", (T,))
+        if grad_entropy is not None:
+            self._check(grad_entropy, (torch.float32,), "grad_entropy", (T,))
+            if entropy is None:
+                raise ValueError("grad_entropy needs the forward's entropy")
+        if entropy is not None:
+            self._check(entropy, (torch.float32,), "entropy", (T,))
+        dev = torch.device("cuda", self.device)
+        need = rlk_logprob_backward_workspace_size(self.config, T, row_chunk)
+        if workspace is not None:
+            self._check(workspace, (torch.uint8, torch.int8), "workspace")
+        if workspace is None or workspace.numel() < need:
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        out = {}
+        if want_hidden:
+            out["grad_hidden"] = torch.empty((T, H), dtype=torch.float32, device=dev)
+        if want_W:
+            if grad_W is None:
+                if accumulate:
+                    raise ValueError("accumulate=True needs grad_W")
+                grad_W = torch.empty((V, H), dtype=torch.float32, device=dev)
+            else:
+                self._check(grad_W, (torch.float32,), "grad_W", (V, H))
+            out["grad_W"] = grad_W
+        s = stream if stream is not None else torch.cuda.current_stream(dev)
+        rlk_logprob_backward(self.handle, hidden.data_ptr(), W.data_ptr(), targets.data_ptr(), T,
+                             None, lse.data_ptr(), _ptr(entropy), grad_logp.data_ptr(),
+                             _ptr(grad_entropy), _ptr(out.get("grad_hidden")),
+                             _ptr(out.get("grad_W")), None,
+                             RLK_BWD_ACCUMULATE if accumulate else 0, row_chunk,
+                             workspace.data_ptr(), workspace.numel(), s.cuda_stream)
+        out["_workspace"] = workspace
+        return out
 
     def merge(self, records, targets, *, status=None, stream=None) -> dict:
         """Merge the records of all segments ([S_c, T, 4] fp32) into logp, lse[, entropy]."""

@@ -27,6 +27,7 @@ RLK_ERR_HIP = 8
 RLK_FLAG_RMSNORM = 1
 RLK_FLAG_ENTROPY = 2
 RLK_FLAG_PORTABLE_EXP = 4
+RLK_BWD_ACCUMULATE = 1
 RLK_DEVICE_STATUS_BAD_TARGET = 1
 
 
@@ -85,6 +86,11 @@ _SIGS = {
                                    _P, _P, _P, ctypes.c_size_t, _S]),
     "rlk_logprob_merge": (_ST, [_H, _P, _P, ctypes.c_int64, _P, _P, _P, _P, _S]),
     "rlk_logprob_device_status": (_ST, [_H, _P, _S, ctypes.POINTER(ctypes.c_uint32)]),
+    "rlk_logprob_backward_workspace_size": (_ST, [ctypes.POINTER(rlk_logprob_config_t),
+                                                  ctypes.c_int64, ctypes.c_int64,
+                                                  ctypes.POINTER(ctypes.c_size_t)]),
+    "rlk_logprob_backward": (_ST, [_H, _P, _P, _P, ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P, _P,
+                                   ctypes.c_uint32, ctypes.c_int64, _P, ctypes.c_size_t, _S]),
     "rlk_logprob_contract_id": (ctypes.c_char_p, [_H]),
     "rlk_build_fingerprint": (ctypes.c_char_p, []),
     "rlk_status_string": (ctypes.c_char_p, [_ST]),
@@ -201,6 +207,24 @@ def rlk_logprob_device_status(handle, workspace, stream) -> int:
     check(load().rlk_logprob_device_status(handle, workspace, stream, ctypes.byref(v)),
           "rlk_logprob_device_status")
     return v.value
+
+
+def rlk_logprob_backward_workspace_size(config: rlk_logprob_config_t, num_rows: int,
+                                        row_chunk: int) -> int:
+    n = ctypes.c_size_t()
+    check(load().rlk_logprob_backward_workspace_size(ctypes.byref(config), num_rows, row_chunk,
+                                                     ctypes.byref(n)),
+          "rlk_logprob_backward_workspace_size")
+    return n.value
+
+
+def rlk_logprob_backward(handle, hidden, W_lm, targets, num_rows, rms_gamma, lse, entropy,
+                         grad_logp, grad_entropy, grad_hidden, grad_W, grad_gamma, flags,
+                         row_chunk, workspace, workspace_bytes, stream) -> None:
+    check(load().rlk_logprob_backward(handle, hidden, W_lm, targets, num_rows, rms_gamma, lse,
+                                      entropy, grad_logp, grad_entropy, grad_hidden, grad_W,
+                                      grad_gamma, flags, row_chunk, workspace, workspace_bytes,
+                                      stream), "rlk_logprob_backward")
 
 
 def rlk_logprob_contract_id(handle) -> str:

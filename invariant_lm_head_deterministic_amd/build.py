@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "librlk_logprob.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["rlk_kernels.hip", "rlk_host.hip"]
+SOURCES = ["rlk_kernels.hip", "rlk_backward.hip", "rlk_host.hip"]
 
 CONTRACT_FLAGS = [
     "-O3",

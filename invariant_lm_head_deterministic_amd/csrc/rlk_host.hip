@@ -611,3 +611,235 @@ RLK_API rlk_status_t rlk_logprob_device_status(rlk_logprob_t h, const void* work
   *flags = v;
   return ok();
 }
+
+// ============================================================================================
+// Backward (B1-B3 in rlk_backward.hip)
+// ============================================================================================
+namespace {
+
+struct BwdMap {
+  int64_t L, Lp, J;    // segment length, padded length, padded vocab width S_c Lp
+  int64_t chunk, Tp;   // rows per chunk, chunk rows padded to kBwdKPad
+  size_t wt, dz, dzt, ht, dpart, total;
+};
+
+BwdMap bwd_map(const rlk_logprob_config_t& c, int64_t rows, int64_t row_chunk, bool want_h,
+               bool want_w) {
+  BwdMap m;
+  const int S = c.vocab_segments;
+  m.L = c.vocab_size / S;
+  m.Lp = (int64_t)round_up((size_t)m.L, rlk::kBwdKPad);
+  m.J = S * m.Lp;
+  const int64_t r = std::max<int64_t>(rows, 1);
+  m.chunk = row_chunk > 0 ? std::min<int64_t>(row_chunk, r) : r;
+  m.Tp = (int64_t)round_up((size_t)m.chunk, rlk::kBwdKPad);
+  const size_t H = (size_t)c.hidden_size;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = round_up(off + bytes, 256);
+    return at;
+  };
+  m.wt = want_h ? take(H * (size_t)m.J * 2) : 0;
+  m.dz = want_h ? take((size_t)m.chunk * (size_t)m.J * 2) : 0;
+  m.dzt = want_w ? take((size_t)m.J * (size_t)m.Tp * 2) : 0;
+  m.ht = want_w ? take(H * (size_t)m.Tp * 2) : 0;
+  m.dpart = (want_h && S > 1) ? take((size_t)S * (size_t)m.chunk * H * 4) : 0;
+  m.total = std::max<size_t>(off, 256);
+  return m;
+}
+
+rlk_status_t check_bwd_rows(const rlk_logprob_config_t& c, int64_t num_rows, int64_t row_chunk) {
+  if (num_rows < 0 || num_rows > 0x7fffffffLL)
+    return fail(RLK_ERR_INVALID_ARGUMENT, "num_rows out of range");
+  if (row_chunk < 0 || (row_chunk > 0 && row_chunk % rlk::kBwdKPad != 0))
+    return fail(RLK_ERR_UNSUPPORTED_SHAPE, "row_chunk %lld is not 0 or a positive multiple of %d",
+                (long long)row_chunk, rlk::kBwdKPad);
+  const BwdMap m = bwd_map(c, num_rows, row_chunk, true, true);
+  // 32-bit buffer ranges of the GEMM tiles: 256 rows of the widest operand
+  if ((int64_t)256 * std::max<int64_t>(m.J, m.Tp) * 2 >= 0x7fffffffLL)
+    return fail(RLK_ERR_UNSUPPORTED_SHAPE, "rows per chunk or padded vocab too large");
+  return RLK_OK;
+}
+
+}  // namespace
+
+RLK_API rlk_status_t rlk_logprob_backward_workspace_size(const rlk_logprob_config_t* config,
+                                                         int64_t num_rows, int64_t row_chunk,
+                                                         size_t* bytes) {
+  if (!bytes) return fail(RLK_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  rlk_status_t st = check_config(config);
+  if (st != RLK_OK) return st;
+  st = check_bwd_rows(*config, num_rows, row_chunk);
+  if (st != RLK_OK) return st;
+  *bytes = bwd_map(*config, num_rows, row_chunk, true, true).total;
+  return ok();
+}
+
+RLK_API rlk_status_t rlk_logprob_backward(rlk_logprob_t h, const void* hidden, const void* W_lm,
+                                          const int32_t* targets, int64_t num_rows,
+                                          const void* rms_gamma, const float* lse,
+                                          const float* entropy, const float* grad_logp,
+                                          const float* grad_entropy, float* grad_hidden,
+                                          float* grad_W, float* grad_gamma, uint32_t flags,
+                                          int64_t row_chunk, void* workspace,
+                                          size_t workspace_bytes, rlk_stream_t stream) {
+  if (!h) return fail(RLK_ERR_INVALID_ARGUMENT, "handle is NULL");
+  const rlk_logprob_config_t& c = h->cfg;
+  if (flags & ~RLK_BWD_ACCUMULATE) return fail(RLK_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", flags);
+  rlk_status_t st = check_bwd_rows(c, num_rows, row_chunk);
+  if (st != RLK_OK) return st;
+  if (c.flags & RLK_FLAG_RMSNORM)
+    return fail(RLK_ERR_UNSUPPORTED_SHAPE, "the backward through the final RMSNorm is not built");
+  if (rms_gamma || grad_gamma)
+    return fail(RLK_ERR_CONTRACT, "rms_gamma / grad_gamma given but RLK_FLAG_RMSNORM not set");
+  const bool want_h = grad_hidden != nullptr, want_w = grad_W != nullptr;
+  if (!want_h && !want_w) return fail(RLK_ERR_INVALID_ARGUMENT, "no gradient requested");
+  if (grad_entropy && !(c.flags & RLK_FLAG_ENTROPY))
+    return fail(RLK_ERR_CONTRACT, "grad_entropy given but RLK_FLAG_ENTROPY not set");
+  if (grad_entropy && !entropy)
+    return fail(RLK_ERR_INVALID_ARGUMENT, "grad_entropy needs the forward's entropy");
+  if (num_rows > 0 && (!hidden || !W_lm || !targets || !lse || !grad_logp))
+    return fail(RLK_ERR_INVALID_ARGUMENT, "hidden, W, targets, lse and grad_logp are required");
+  if (!W_lm && want_w) return fail(RLK_ERR_INVALID_ARGUMENT, "W is required");
+  if (!aligned16(hidden) || !aligned16(W_lm) || !aligned16(targets) || !aligned16(lse) ||
+      !aligned16(grad_logp) || !aligned16(entropy) || !aligned16(grad_entropy) ||
+      !aligned16(grad_hidden) || !aligned16(grad_W) || !aligned16(workspace))
+    return fail(RLK_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
+  const BwdMap m = bwd_map(c, num_rows, row_chunk, want_h, want_w);
+  if (!workspace || workspace_bytes < m.total)
+    return fail(RLK_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", m.total,
+                workspace_bytes);
+  DeviceGuard guard(h->device);
+  if (guard.err != hipSuccess) return hip_fail(guard.err, "hipSetDevice");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool accumulate = flags & RLK_BWD_ACCUMULATE;
+  const int S = c.vocab_segments;
+  const int H = c.hidden_size;
+  const int64_t V = c.vocab_size;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  hipError_t e;
+  if (num_rows == 0) {
+    if (want_w && !accumulate) {
+      e = rlk::launch_zero_f32(grad_W, V * H, s);
+      if (e != hipSuccess) return hip_fail(e, "zero launch");
+    }
+    return ok();
+  }
+  uint16_t* WT = reinterpret_cast<uint16_t*>(ws + m.wt);
+  uint16_t* dz = reinterpret_cast<uint16_t*>(ws + m.dz);
+  uint16_t* dzt = reinterpret_cast<uint16_t*>(ws + m.dzt);
+  uint16_t* hT = reinterpret_cast<uint16_t*>(ws + m.ht);
+  float* dpart = reinterpret_cast<float*>(ws + m.dpart);
+  const uint16_t* hid = static_cast<const uint16_t*>(hidden);
+  const uint16_t* Wb = static_cast<const uint16_t*>(W_lm);
+  if (want_h) {
+    rlk::TransposeArgs ta;
+    ta.in = Wb;
+    ta.ldi = H;
+    ta.R = V;
+    ta.C = H;
+    ta.out = WT;
+    ta.ldo = m.J;
+    ta.J = m.J;
+    ta.L = m.L;
+    ta.Lp = m.Lp;
+    e = rlk::launch_transpose(ta, s);
+    if (e != hipSuccess) return hip_fail(e, "transpose launch");
+  }
+  int64_t chunk_no = 0;
+  for (int64_t r0 = 0; r0 < num_rows; r0 += m.chunk, ++chunk_no) {
+    const int64_t r1 = std::min<int64_t>(num_rows, r0 + m.chunk);
+    const int64_t n = r1 - r0;
+    const int64_t np = (int64_t)round_up((size_t)n, rlk::kBwdKPad);
+    // B1: dz and its transpose
+    rlk::GemmArgs a{};
+    a.A = Wb;
+    a.lda = H;
+    a.B = hid + r0 * H;
+    a.ldb = H;
+    a.M = (int32_t)V;
+    a.N = (int32_t)n;
+    a.K = H;
+    a.seg_len = m.L;
+    a.seg_pad = m.Lp;
+    a.targets = targets + r0;
+    a.lse = lse + r0;
+    a.ent = grad_entropy ? entropy + r0 : nullptr;
+    a.g = grad_logp + r0;
+    a.gH = grad_entropy ? grad_entropy + r0 : nullptr;
+    a.dz = want_h ? dz : nullptr;
+    a.lddz = m.J;
+    a.dzt = want_w ? dzt : nullptr;
+    a.lddzt = np;
+    a.V = V;
+    a.inv_tau = c.inv_temperature;
+    a.portable = (c.flags & RLK_FLAG_PORTABLE_EXP) ? 1 : 0;
+    e = rlk::launch_gemm_dz(a, s);
+    if (e != hipSuccess) return hip_fail(e, "dz launch");
+    for (int sg = 0; sg < S && m.Lp > m.L; ++sg) {
+      const int64_t p0 = sg * m.Lp + m.L, p1 = (sg + 1) * m.Lp;
+      if (want_h) e = rlk::launch_zero_rect(dz, m.J, 0, n, p0, p1, s);
+      if (e == hipSuccess && want_w) e = rlk::launch_zero_rect(dzt, np, p0, p1, 0, np, s);
+      if (e != hipSuccess) return hip_fail(e, "pad launch");
+    }
+    if (want_w && np > n) {
+      e = rlk::launch_zero_rect(dzt, np, 0, m.J, n, np, s);
+      if (e != hipSuccess) return hip_fail(e, "pad launch");
+    }
+    if (want_h) {
+      // B2: per segment chains, then the segment tree
+      rlk::GemmArgs g{};
+      g.A = WT;
+      g.lda = m.J;
+      g.a_batch = m.Lp;
+      g.B = dz;
+      g.ldb = m.J;
+      g.b_batch = m.Lp;
+      g.M = H;
+      g.N = (int32_t)n;
+      g.K = (int32_t)m.Lp;
+      g.C = S > 1 ? dpart : grad_hidden + r0 * H;
+      g.ldc = H;
+      g.c_batch = n * H;
+      e = rlk::launch_gemm_out(g, S, s);
+      if (e != hipSuccess) return hip_fail(e, "dh launch");
+      if (S > 1) {
+        e = rlk::launch_seg_tree(dpart, n * H, S, grad_hidden + r0 * H, n * H, s);
+        if (e != hipSuccess) return hip_fail(e, "dh tree launch");
+      }
+    }
+    if (want_w) {
+      // B3: the chain over rows continues from the previous chunk
+      rlk::TransposeArgs ta;
+      ta.in = hid + r0 * H;
+      ta.ldi = H;
+      ta.R = n;
+      ta.C = H;
+      ta.out = hT;
+      ta.ldo = np;
+      ta.J = np;
+      ta.L = n;
+      ta.Lp = np;
+      e = rlk::launch_transpose(ta, s);
+      if (e != hipSuccess) return hip_fail(e, "transpose launch");
+      rlk::GemmArgs g{};
+      g.A = hT;
+      g.lda = np;
+      g.B = dzt;
+      g.ldb = np;
+      g.M = H;
+      g.N = (int32_t)m.J;
+      g.K = (int32_t)np;
+      g.seg_len = m.L;
+      g.seg_pad = m.Lp;
+      g.C = grad_W;
+      g.ldc = H;
+      g.accumulate = (accumulate || chunk_no > 0) ? 1 : 0;
+      g.map_rows = 1;
+      e = rlk::launch_gemm_out(g, 1, s);
+      if (e != hipSuccess) return hip_fail(e, "dW launch");
+    }
+  }
+  return ok();
+}

@@ -88,6 +88,69 @@ struct RmsArgs {
   int32_t portable;         // RSQ as a correctly rounded 1/sqrt (C11p)
 };
 
+// ---- backward ----
+constexpr int kBwdKPad = 128;  // K of the backward GEMMs (vocab per segment, rows) padded to this
+
+// NT GEMM tile kernel of the backward: acc[m, n] = sum_k A[m, k] B[n, k] (bf16, fp32 MFMA chain,
+// K ascending from +0 or from the stored output), then one of two epilogues.
+//  DZ:  A = W rows (m = vocab v), B = LM-head input rows (n = row t), K = H. Writes the bf16
+//       gradient of the tempered logits' loss (B1) to dz[t][col(v)] and dzt[col(v)][t].
+//  OUT: writes C[row(n) * ldc + m] in fp32 (dh: m = h, n = t; dW: m = h, n = padded vocab row).
+// col(v) / row(n) is the segment-padded vocab layout: v = s seg_len + c <-> s seg_pad + c.
+struct GemmArgs {
+  const uint16_t* A;
+  int64_t lda;
+  const uint16_t* B;
+  int64_t ldb;
+  int32_t M, N, K;          // K: a multiple of kBwdKPad
+  int64_t seg_len;          // L = V / S_c (segment-padded vocab layout)
+  int64_t seg_pad;          // Lp = L rounded up to kBwdKPad
+  // OUT
+  float* C;
+  int64_t ldc;
+  int64_t c_batch;          // C offset per blockIdx.y (one vocab segment per y for dh)
+  int64_t a_batch, b_batch; // A / B offsets per blockIdx.y
+  int32_t accumulate;       // start the chain from C's stored values
+  int32_t map_rows;         // OUT rows n are segment-padded vocab rows (skip padding rows)
+  // DZ
+  const int32_t* targets;   // [rows]
+  const float* lse;         // forward lse [rows]
+  const float* ent;         // forward entropy [rows] (with grad_ent)
+  const float* g;           // dL/dlogp [rows]
+  const float* gH;          // dL/dentropy [rows] or null
+  uint16_t* dz;             // bf16 [rows][S_c Lp] or null
+  int64_t lddz;
+  uint16_t* dzt;            // bf16 [S_c Lp][lddzt] or null
+  int64_t lddzt;
+  int64_t V;
+  float inv_tau;
+  int32_t portable;
+};
+
+// out[c][j] (bf16, row stride ldo) = in[r(j)][c] for the segment-padded column j of row r(j)
+// (j = s Lp + cc, r = s L + cc, cc < L, r < R), else +0; c < C, j < J.
+struct TransposeArgs {
+  const uint16_t* in;
+  int64_t ldi;
+  int64_t R, C;
+  uint16_t* out;
+  int64_t ldo;
+  int64_t J;
+  int64_t L, Lp;
+};
+
+hipError_t launch_gemm_dz(const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_out(const GemmArgs& a, int batches, hipStream_t s);
+hipError_t launch_transpose(const TransposeArgs& a, hipStream_t s);
+// bf16 zeros over rows [r0, r1) x columns [c0, c1) of a matrix with row stride ld
+hipError_t launch_zero_rect(uint16_t* p, int64_t ld, int64_t r0, int64_t r1, int64_t c0,
+                            int64_t c1, hipStream_t s);
+// fp32 zeros over n elements (a fill kernel: usable under graph capture)
+hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
+// out[i] = balanced pairwise tree over s < nseg of part[s * stride + i] (nseg in 1, 2, 4, 8)
+hipError_t launch_seg_tree(const float* part, int64_t stride, int nseg, float* out, int64_t n,
+                           hipStream_t s);
+
 // Token-tile widths the LM-head kernel can be forced to (0 = chosen per launch).
 bool token_tile_supported(int bt);
 

@@ -158,3 +158,21 @@ def test_flag_bits(lib):
     with pytest.raises(_lib.RlkError) as e:
         _ws(bad, l)
     assert e.value.status == _lib.RLK_ERR_INVALID_ARGUMENT
+
+
+def test_backward_workspace_size(lib):
+    cfg = make_config(4096, 151936, vocab_segments=4)
+    n = _lib.rlk_logprob_backward_workspace_size(cfg, 4096, 0)
+    Lp = 38016  # 37984 rounded up to 128
+    J = 4 * Lp
+    want = 4096 * J * 2 + 4096 * J * 2 + J * 4096 * 2 + 4096 * 4096 * 2 + 4 * 4096 * 4096 * 4
+    assert want <= n < want + 6 * 256
+    # chunked: the per-chunk buffers shrink, the transposed W does not
+    m = _lib.rlk_logprob_backward_workspace_size(cfg, 4096, 1024)
+    assert m < n and m >= 4096 * J * 2
+    for bad in (100, -128):
+        with pytest.raises(_lib.RlkError) as e:
+            _lib.rlk_logprob_backward_workspace_size(cfg, 4096, bad)
+        assert e.value.status in (_lib.RLK_ERR_UNSUPPORTED_SHAPE, _lib.RLK_ERR_INVALID_ARGUMENT)
+    with pytest.raises(_lib.RlkError):
+        _lib.rlk_logprob_backward_workspace_size(cfg, -1, 0)

@@ -1,0 +1,179 @@
+"""The backward (B1-B3) through the C ABI: parity with the float64 backward oracle, and bitwise
+invariance of the gradients across row chunks, gradient accumulation and row order.
+
+Parity bar, from the arithmetic: the one modelled rounding point is dz in bf16 (the oracle rounds
+its float64 dz, the library its fp32 dz). The two roundings can land on neighbouring bf16 values
+when the exact value sits near a rounding boundary, a difference of at most one bf16 step,
+2^-7 |dz|; the fp32 MFMA chains add at most K/32 roundings of 2^-24 relative to the sum of
+|terms|. So every element must satisfy
+    |g_gpu - g_oracle| <= (2^-7 + 1e-4) (|dz| @ |W|)   for dh,  (|dz|^T @ |h|) for dW,
+and the relative Frobenius error must stay under 1e-3 (flips are rare: it is ~1e-6 in practice).
+"""
+
+import numpy as np
+import pytest
+
+import datagen
+import oracle
+from tests.helpers import assert_bitwise, dev_bits, dev_i32, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(T, H, V, cfg, pad_every=0):
+    h, W, y = datagen.small_case(T, H, V, cfg)
+    if pad_every:
+        y[::pad_every] = -1
+    g = np.random.default_rng(cfg).normal(size=T).astype(np.float32)
+    gH = np.random.default_rng(cfg + 1).normal(size=T).astype(np.float32)
+    return h, W, y, g, gH
+
+
+def _run(rlk, h, W, y, g, gH=None, *, S=4, tau=1.0, portable=False, **kw):
+    import torch
+
+    T, H = h.shape
+    V = W.shape[0]
+    ent = gH is not None
+    lp = rlk.Logprob(H, V, vocab_segments=S, temperature=tau, entropy=ent, portable=portable)
+    hd, Wd, yd = dev_bits(h), dev_bits(W), dev_i32(y)
+    fw = lp.forward(hd, Wd, yd)
+    gd = torch.from_numpy(g).cuda()
+    gHd = None if gH is None else torch.from_numpy(gH).cuda()
+    out = lp.backward(hd, Wd, yd, fw["lse"], gd, entropy=fw.get("entropy"), grad_entropy=gHd,
+                      **kw)
+    torch.cuda.synchronize()
+    return {k: host(v) for k, v in out.items() if not k.startswith("_")}, (lp, hd, Wd, yd, fw, gd,
+                                                                            gHd)
+
+
+def _check(got, h, W, y, g, gH, tau, rows_h=None, rows_w=None):
+    hf = oracle.bf16_bits_to_f64(h)
+    Wf = oracle.bf16_bits_to_f64(W)
+    want = oracle.grads(h, W, y, g, gH, tau=tau, dh_rows=rows_h, dW_rows=rows_w)
+    dz = np.abs(oracle.dlogits(hf @ Wf.T / tau, y, g, gH, tau))
+    rh = np.arange(h.shape[0]) if rows_h is None else rows_h
+    rw = np.arange(W.shape[0]) if rows_w is None else rows_w
+    for key, ref, bound in (("grad_hidden", want["dh"], dz[rh] @ np.abs(Wf)),
+                            ("grad_W", want["dW"], dz[:, rw].T @ np.abs(hf))):
+        gg = got[key][rh] if key == "grad_hidden" else got[key][rw]
+        d = np.abs(gg.astype(np.float64) - ref)
+        lim = (2.0 ** -7 + 1e-4) * bound + 1e-30
+        fro = np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-300)
+        print(key, "max", float(d.max()), "max/lim", float((d / lim).max()), "fro", fro, flush=True)
+        assert np.all(d <= lim), (key, float((d / lim).max()))
+        assert fro <= 1e-3, (key, fro)
+
+
+CASES = [
+    # T, H, V, S_c, tau, entropy gradient, pad every
+    (300, 256, 5000, 4, 1.0, False, 0),   # 3 row tiles, segments of 1250 (Lp 1280)
+    (77, 384, 3000, 2, 0.7, True, 5),     # temperature, entropy gradient, padded rows
+    (33, 128, 1000, 1, 1.0, True, 0),     # one segment: no tree
+    (130, 256, 5600, 8, 1.0, False, 7),   # 8 segments of 700 (Lp 768)
+    (1, 128, 1000, 4, 1.0, False, 0),     # a single row, segments of 250 (not a multiple of 4)
+]
+
+
+@pytest.mark.parametrize("T,H,V,S,tau,ent,pad", CASES)
+def test_backward_matches_oracle(rlk, T, H, V, S, tau, ent, pad):
+    h, W, y, g, gH = _inputs(T, H, V, 500 + T, pad)
+    say(f"backward T={T} H={H} V={V} S={S} tau={tau} ent={ent}")
+    got, _ = _run(rlk, h, W, y, g, gH if ent else None, S=S, tau=tau)
+    _check(got, h, W, y, g, gH if ent else None, tau)
+
+
+def test_backward_portable_matches_oracle(rlk):
+    T, H, V = 150, 256, 3000
+    h, W, y, g, gH = _inputs(T, H, V, 520, 9)
+    say("backward portable")
+    got, _ = _run(rlk, h, W, y, g, gH, S=4, tau=0.8, portable=True)
+    _check(got, h, W, y, g, gH, 0.8)
+
+
+def test_backward_chunks_accumulation_and_order_are_bitwise_invariant(rlk):
+    import torch
+
+    T, H, V = 300, 256, 4000
+    h, W, y, g, gH = _inputs(T, H, V, 530, 11)
+    say("backward invariances")
+    one, (lp, hd, Wd, yd, fw, gd, gHd) = _run(rlk, h, W, y, g, gH, S=4)
+    ent = fw["entropy"]
+    for rc in (128, 256):
+        o = lp.backward(hd, Wd, yd, fw["lse"], gd, entropy=ent, grad_entropy=gHd, row_chunk=rc)
+        torch.cuda.synchronize()
+        assert_bitwise(o["grad_hidden"], one["grad_hidden"], f"dh chunk {rc}")
+        assert_bitwise(o["grad_W"], one["grad_W"], f"dW chunk {rc}")
+    # two micro-batches: rows [0, 256) then [256, 300) accumulated into the same grad_W
+    gw = torch.empty((V, H), dtype=torch.float32, device="cuda")
+    a = lp.backward(hd[:256].contiguous(), Wd, yd[:256].contiguous(), fw["lse"][:256].contiguous(),
+                    gd[:256].contiguous(), entropy=ent[:256].contiguous(),
+                    grad_entropy=gHd[:256].contiguous(), grad_W=gw)
+    b = lp.backward(hd[256:].contiguous(), Wd, yd[256:].contiguous(), fw["lse"][256:].contiguous(),
+                    gd[256:].contiguous(), entropy=ent[256:].contiguous(),
+                    grad_entropy=gHd[256:].contiguous(), grad_W=gw, accumulate=True)
+    torch.cuda.synchronize()
+    assert_bitwise(gw, one["grad_W"], "dW accumulated")
+    assert_bitwise(torch.cat([a["grad_hidden"], b["grad_hidden"]]), one["grad_hidden"], "dh split")
+    # rows are independent in dh: a permutation permutes it
+    perm = np.random.default_rng(4).permutation(T)
+    pt = torch.from_numpy(perm).cuda()
+    o = lp.backward(hd[pt].contiguous(), Wd, yd[pt].contiguous(), fw["lse"][pt].contiguous(),
+                    gd[pt].contiguous(), entropy=ent[pt].contiguous(),
+                    grad_entropy=gHd[pt].contiguous(), want_W=False)
+    torch.cuda.synchronize()
+    assert_bitwise(host(o["grad_hidden"]), one["grad_hidden"][perm], "dh permuted")
+    # run to run
+    o = lp.backward(hd, Wd, yd, fw["lse"], gd, entropy=ent, grad_entropy=gHd)
+    torch.cuda.synchronize()
+    assert_bitwise(o["grad_hidden"], one["grad_hidden"], "dh repeat")
+    assert_bitwise(o["grad_W"], one["grad_W"], "dW repeat")
+
+
+def test_backward_only_one_gradient(rlk):
+    T, H, V = 64, 128, 1000
+    h, W, y, g, _ = _inputs(T, H, V, 540)
+    say("backward single outputs")
+    both, (lp, hd, Wd, yd, fw, gd, _) = _run(rlk, h, W, y, g)
+    import torch
+
+    oh = lp.backward(hd, Wd, yd, fw["lse"], gd, want_W=False)
+    ow = lp.backward(hd, Wd, yd, fw["lse"], gd, want_hidden=False)
+    torch.cuda.synchronize()
+    assert "grad_W" not in oh and "grad_hidden" not in ow
+    assert_bitwise(oh["grad_hidden"], both["grad_hidden"], "dh alone")
+    assert_bitwise(ow["grad_W"], both["grad_W"], "dW alone")
+
+
+def test_backward_refusals(rlk):
+    import torch
+
+    H, V = 128, 1000
+    h, W, y, g, gH = _inputs(8, H, V, 550)
+    hd, Wd, yd = dev_bits(h), dev_bits(W), dev_i32(y)
+    lse = torch.zeros(8, dtype=torch.float32, device="cuda")
+    gd = torch.from_numpy(g).cuda()
+    lp = rlk.Logprob(H, V, rmsnorm=True)
+    with pytest.raises(rlk.RlkError):
+        lp.backward(hd, Wd, yd, lse, gd)
+    lp = rlk.Logprob(H, V)  # no entropy flag
+    with pytest.raises(rlk.RlkError):
+        lp.backward(hd, Wd, yd, lse, gd, entropy=lse, grad_entropy=torch.from_numpy(gH).cuda())
+    with pytest.raises(rlk.RlkError):
+        lp.backward(hd, Wd, yd, lse, gd, row_chunk=100)
+    with pytest.raises(ValueError):
+        lp.backward(hd, Wd, yd, lse[:4], gd)
+
+
+def test_backward_full_size_sampled(rlk):
+    """Qwen3-8B head shape (T=4096, H=4096, V=151936, 4 segments): sampled rows of dh and of dW
+    against the oracle (which still reduces over every row and every vocab index)."""
+    w = datagen.WORKLOADS["qwen3_8b_head"]
+    h, W = datagen.hidden_bits(w), datagen.weight_bits(w)
+    y = np.load("tests/golden/targets_qwen3_8b_head.npy").astype(np.int32)
+    g = np.random.default_rng(560).normal(size=w.T).astype(np.float32)
+    say("backward full size")
+    got, _ = _run(rlk, h, W, y, g, S=w.segments)
+    rows_h = np.array([0, 1, 777, 2048, 4095])
+    rows_w = np.concatenate([y[[0, 777]], [0, 37983, 37984, 75968, 151935]])
+    _check(got, h, W, y, g, None, 1.0, rows_h=rows_h, rows_w=rows_w)
