@@ -14,7 +14,7 @@ computes the unsplit reduction. Parity status of each function is stated in its 
 ``oracle.logprob.PINS``.
 """
 
-from .backward import dlogits, grads  # noqa: F401
+from .backward import dlogits, grads, rmsnorm_backward  # noqa: F401
 from .backward import PINS as BACKWARD_PINS  # noqa: F401
 from .logprob import (  # noqa: F401
     PINS,

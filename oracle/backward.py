@@ -26,7 +26,12 @@ from __future__ import annotations
 
 import numpy as np
 
-from .logprob import bf16_bits_to_f64, entropy_rows, logsumexp_rows, round_to_bf16
+from .logprob import bf16_bits_to_f64, entropy_rows, logsumexp_rows, rmsnorm_bf16, round_to_bf16
+
+PINS_RMS = {
+    "rmsnorm_backward": "torch CPU float64 autograd through x gamma / sqrt(mean x^2 + eps); central "
+                        "finite differences; a row x = c (constant) closed form",
+}
 
 PINS = {
     "dlogits": "central finite differences of the forward oracle; torch CPU float64 autograd of "
@@ -65,17 +70,45 @@ def dlogits(zp: np.ndarray, targets: np.ndarray, g: np.ndarray, gH: np.ndarray |
     return out
 
 
+def rmsnorm_backward(x: np.ndarray, gamma: np.ndarray, eps: float, dy: np.ndarray):
+    """(dx, dgamma) of y = x gamma / sqrt(mean_k x_k^2 + eps), given dy (float64, per row).
+
+    With r = (mean x^2 + eps)^(-1/2) and c = sum_j dy_j gamma_j x_j:
+        dx_k = r gamma_k dy_k - x_k r^3 c / H,      dgamma_k = sum_t dy_tk x_tk r_t.
+    The bf16 rounding of y in the forward is passed straight through (its derivative is taken
+    as 1), as the library does.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    H = x.shape[1]
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=1) + eps)
+    c = np.sum(dy * gamma[None, :] * x, axis=1)
+    dx = (r[:, None] * gamma[None, :] * dy) - x * (r ** 3 * c / H)[:, None]
+    dgamma = np.sum(dy * x * r[:, None], axis=0)
+    return dx, dgamma
+
+
 def grads(hidden: np.ndarray, W: np.ndarray, targets: np.ndarray, grad_logp: np.ndarray,
           grad_entropy: np.ndarray | None = None, tau: float = 1.0, round_dz: bool = True,
           dh_rows: np.ndarray | None = None, dW_rows: np.ndarray | None = None,
-          row_chunk: int = 256) -> dict:
-    """dh [T, H] (w.r.t. the LM-head input) and dW [V, H] of L, in float64.
+          row_chunk: int = 256, gamma_bits: np.ndarray | None = None, rms_eps: float = 1e-6,
+          round_y: bool = True) -> dict:
+    """dh [T, H] and dW [V, H] of L (and dgamma [H] with the RMSNorm), in float64.
 
     hidden: bf16 bits [T, H] or float64 values; W: bf16 bits [V, H] or float64 values.
+    gamma_bits: apply the final RMSNorm first (as the forward oracle does, its output rounded to
+    bf16 unless ``round_y`` is False); dh is then the gradient with respect to the RMSNorm's
+    input x, and dW is taken against the normed rows.
     dh_rows / dW_rows: evaluate only those rows of dh / of dW (all rows still enter every lse
     and every dW sum). Rows are processed in chunks of ``row_chunk`` to bound memory.
     """
-    h = _f64(hidden)
+    x = _f64(hidden)
+    gamma = None if gamma_bits is None else _f64(gamma_bits)
+    if gamma is None:
+        h = x
+    elif round_y:
+        h = rmsnorm_bf16(x, gamma, rms_eps)
+    else:
+        h = x * gamma[None, :] / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + rms_eps)
     Wf = _f64(W)
     y = np.asarray(targets, dtype=np.int64)
     g = np.asarray(grad_logp, dtype=np.float64)
@@ -83,6 +116,8 @@ def grads(hidden: np.ndarray, W: np.ndarray, targets: np.ndarray, grad_logp: np.
     T, H = h.shape
     V = Wf.shape[0]
     rows_h = np.arange(T) if dh_rows is None else np.asarray(dh_rows, dtype=np.int64)
+    if gamma is not None and dh_rows is not None:
+        rows_h = np.arange(T)  # dgamma sums over every row
     rows_w = np.arange(V) if dW_rows is None else np.asarray(dW_rows, dtype=np.int64)
     dh = np.zeros((rows_h.size, H))
     dW = np.zeros((rows_w.size, H))
@@ -100,4 +135,9 @@ def grads(hidden: np.ndarray, W: np.ndarray, targets: np.ndarray, grad_logp: np.
         if sel.size:
             dh[pos_h[r0 + sel]] = dz[sel] @ Wf
         dW += dz[:, rows_w].T @ h[r0:r1]
-    return {"dh": dh, "dW": dW}
+    if gamma is None:
+        return {"dh": dh, "dW": dW}
+    dx, dgamma = rmsnorm_backward(x, gamma, rms_eps, dh)
+    if dh_rows is not None:
+        dx = dx[np.asarray(dh_rows, dtype=np.int64)]
+    return {"dh": dx, "dW": dW, "dgamma": dgamma}

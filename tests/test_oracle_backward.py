@@ -120,3 +120,76 @@ def test_row_subsets_equal_the_full_result():
     sub = oracle.grads(h, W, y, gl, ge, dh_rows=np.array([0, 5, 8]), dW_rows=np.array([3, 39]))
     np.testing.assert_allclose(sub["dh"], full["dh"][[0, 5, 8]], rtol=1e-14, atol=1e-16)
     np.testing.assert_allclose(sub["dW"], full["dW"][[3, 39]], rtol=1e-14, atol=1e-16)
+
+
+def _rms_case(T, H, V, seed):
+    g = np.random.default_rng(seed)
+    x = g.normal(size=(T, H))
+    gamma = 1.0 + 0.1 * g.normal(size=H)
+    W = g.normal(size=(V, H)) * 0.3
+    y = g.integers(0, V, size=T)
+    return x, gamma, W, y, g.normal(size=T), g.normal(size=T)
+
+
+def test_rmsnorm_grads_match_torch_autograd():
+    torch = pytest.importorskip("torch")
+    T, H, V, tau, eps = 6, 16, 30, 0.7, 1e-3
+    x, gamma, W, y, gl, ge = _rms_case(T, H, V, 11)
+    y[2] = -1
+    xt = torch.tensor(x, requires_grad=True)
+    gt = torch.tensor(gamma, requires_grad=True)
+    Wt = torch.tensor(W, requires_grad=True)
+    hn = xt * gt / torch.sqrt((xt * xt).mean(dim=1, keepdim=True) + eps)
+    lsm = torch.log_softmax((hn @ Wt.T) / tau, dim=1)
+    act = torch.tensor(y >= 0)
+    yy = torch.tensor(np.where(y >= 0, y, 0))
+    L = (torch.tensor(gl) * lsm[torch.arange(T), yy] * act).sum() \
+        + (torch.tensor(ge) * -(lsm.exp() * lsm).sum(dim=1) * act).sum()
+    L.backward()
+    got = oracle.grads(x, W, y, gl, ge, tau=tau, round_dz=False, gamma_bits=gamma, rms_eps=eps,
+                       round_y=False)
+    np.testing.assert_allclose(got["dh"], xt.grad.numpy(), rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(got["dW"], Wt.grad.numpy(), rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(got["dgamma"], gt.grad.numpy(), rtol=1e-11, atol=1e-13)
+
+
+def test_rmsnorm_backward_central_differences():
+    T, H, eps = 3, 5, 1e-2
+    g = np.random.default_rng(12)
+    x = g.normal(size=(T, H))
+    gamma = 1.0 + 0.2 * g.normal(size=H)
+    dy = g.normal(size=(T, H))
+
+    def f(xx, gg):
+        yv = xx * gg[None, :] / np.sqrt(np.mean(xx * xx, axis=1, keepdims=True) + eps)
+        return float(np.sum(dy * yv))
+
+    dx, dgam = oracle.rmsnorm_backward(x, gamma, eps, dy)
+    e = 1e-6
+    for arr, want in ((x, dx), (gamma, dgam)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            old = arr[idx]
+            arr[idx] = old + e
+            fp = f(x, gamma)
+            arr[idx] = old - e
+            fm = f(x, gamma)
+            arr[idx] = old
+            num[idx] = (fp - fm) / (2 * e)
+        np.testing.assert_allclose(want, num, rtol=1e-6, atol=1e-9)
+
+
+def test_rmsnorm_backward_constant_row():
+    # a constant row x = c 1 with eps = 0 gives y = gamma sign(c): r = 1/|c|, so with dy = 1,
+    # dx_k = gamma_k / |c| - c r^3 (c sum gamma) / H and dgamma_k = sign(c); y does not change
+    # when x is scaled, so dx is orthogonal to x.
+    H = 6
+    gamma = np.linspace(0.5, 1.5, H)
+    x = np.full((1, H), -3.0)
+    dy = np.ones((1, H))
+    dx, dgam = oracle.rmsnorm_backward(x, gamma, 0.0, dy)
+    # r = 1/3; c = -3 sum(gamma); dx_k = gamma_k/3 - (-3)(1/27)(-3 sum gamma)/H
+    want = gamma / 3 - np.sum(gamma) / (3 * H)
+    np.testing.assert_allclose(dx[0], want, rtol=1e-14)
+    np.testing.assert_allclose(dgam, -np.ones(H), rtol=1e-14)
+    assert abs(np.dot(dx[0], np.ones(H))) < 1e-13  # scaling x leaves y unchanged
