@@ -380,6 +380,35 @@ def long_grpo(rlk, datagen, np, torch, Wd) -> dict:
     return out
 
 
+def backward(rlk, np, torch, hd, Wd, yd, w, steps: int = 5, warmup: int = 2) -> dict:
+    """The backward at the headline shape: gradients of sum_t logp_t with respect to the hidden
+    rows and W (dz GEMM with its epilogue, W transpose, per-segment dh GEMM + tree, dW GEMM),
+    timed on the stream with torch events; TFLOP/s counts the three GEMMs (3 x 2 T H V)."""
+    dev = hd.device
+    lp = rlk.Logprob(w.H, w.V, vocab_segments=w.segments, device=0)
+    fw = lp.forward(hd, Wd, yd)
+    g = torch.ones(w.T, dtype=torch.float32, device=dev)
+    gw = torch.empty((w.V, w.H), dtype=torch.float32, device=dev)
+    ws = None
+    for _ in range(warmup):
+        ws = lp.backward(hd, Wd, yd, fw["lse"], g, grad_W=gw, workspace=ws)["_workspace"]
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        lp.backward(hd, Wd, yd, fw["lse"], g, grad_W=gw, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    fl = 3 * 2.0 * w.T * w.H * w.V
+    del lp, ws, gw
+    return {"ms_per_step": ms, "tokens_per_s": w.T / (ms * 1e-3),
+            "gemm_tflops": fl / (ms * 1e-3) / 1e12,
+            "frac_of_bf16_peak": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "workspace_bytes": rlk.rlk_logprob_backward_workspace_size(
+                rlk.make_config(w.H, w.V, w.segments), w.T, 0)}
+
+
 def extras(rlk, datagen, np, torch, hd, Wd, yd, w, ref_logp) -> dict:
     """The other rows of the path, measured next to the headline: the rollout layout of the TP4
     workload (decode batches x 4 vocab shards; HBM-bound W stream), the same batch with the
@@ -410,6 +439,8 @@ def extras(rlk, datagen, np, torch, hd, Wd, yd, w, ref_logp) -> dict:
         "max_abs_diff_logp_vs_default": float(np.max(np.abs(
             r["_logp"].astype(np.float64) - ref_logp.astype(np.float64))))}
     del lpp
+    log("extras: backward")
+    out["backward_one_pass"] = backward(rlk, np, torch, hd, Wd, yd, w)
     log("extras: torch-native reference path")
     out["torch_native_lm_head"] = torch_native(np, torch, hd, Wd, yd, sizes, ref_logp)
     log("extras: long_grpo inputs")

@@ -199,13 +199,17 @@ const char* rlk_logprob_contract_id(rlk_logprob_t handle);
  *  B3 grad_W = one fp32 MFMA chain over rows ascending (32 at a time, rows padded with zeros to a
  *     multiple of 128), from 0 or, with RLK_BWD_ACCUMULATE, continuing from grad_W's contents;
  *     any row_chunk (a multiple of 128) therefore gives the bits of one pass.
- * The final RMSNorm's backward is not built: a handle with RLK_FLAG_RMSNORM is refused. */
-#define RLK_BWD_ACCUMULATE 1u /* grad_W continues the chain from its current contents */
+ *  B4 with RLK_FLAG_RMSNORM, B1-B3 run on the RMSNorm's bf16 output (recomputed bit for bit)
+ *     and grad_hidden is taken through the RMSNorm (its bf16 rounding passed straight through):
+ *     dx = (dy gamma) r - x (c r^3 / H), c = sum (dy gamma) x in the forward's reduction order;
+ *     grad_gamma = sum over rows of (dy x) r, as a chain over groups of 128 rows (from 0 or,
+ *     with RLK_BWD_ACCUMULATE, from grad_gamma's contents). */
+#define RLK_BWD_ACCUMULATE 1u /* grad_W / grad_gamma continue their chains from their contents */
 
 /* Workspace bytes for rlk_logprob_backward with both gradients requested (an upper bound for
  * fewer). row_chunk: 0 (all rows at once) or a positive multiple of 128. About
  * 2 V_pad (H + 2 rows_per_chunk) + 4 S_c rows_per_chunk H bytes (V_pad = V rounded up per
- * segment to 128). */
+ * segment to 128), plus about 6 rows_per_chunk H bytes with RLK_FLAG_RMSNORM. */
 rlk_status_t rlk_logprob_backward_workspace_size(const rlk_logprob_config_t* config,
                                                  int64_t num_rows, int64_t row_chunk,
                                                  size_t* bytes);
@@ -213,8 +217,9 @@ rlk_status_t rlk_logprob_backward_workspace_size(const rlk_logprob_config_t* con
 /* hidden bf16 [T, H], W_lm bf16 [V, H], targets int32 [T] (negative = padded): the forward's
  * inputs. lse fp32 [T] and (with grad_entropy) entropy fp32 [T]: the forward's outputs for these
  * rows under this handle. grad_logp fp32 [T]; grad_entropy fp32 [T] or NULL (needs
- * RLK_FLAG_ENTROPY). Outputs (each optional, at least one): grad_hidden fp32 [T, H],
- * grad_W fp32 [V, H]; rms_gamma and grad_gamma must be NULL. flags: RLK_BWD_ACCUMULATE or 0.
+ * RLK_FLAG_ENTROPY). rms_gamma bf16 [H]: required with RLK_FLAG_RMSNORM, else NULL. Outputs
+ * (each optional, at least one): grad_hidden fp32 [T, H], grad_W fp32 [V, H], grad_gamma fp32
+ * [H] (RLK_FLAG_RMSNORM only). flags: RLK_BWD_ACCUMULATE (grad_W and grad_gamma continue) or 0.
  * All device pointers 16-byte aligned; the workspace (device, caller-owned) at least
  * rlk_logprob_backward_workspace_size() bytes. Enqueues on stream without synchronizing or
  * allocating. Errors are returned before anything is enqueued. */

@@ -231,13 +231,15 @@ class Logprob:
         return records
 
     def backward(self, hidden, W, targets, lse, grad_logp, *, entropy=None, grad_entropy=None,
-                 want_hidden: bool = True, want_W: bool = True, grad_W=None,
+                 gamma=None, want_hidden: bool = True, want_W: bool = True,
+                 want_gamma: bool | None = None, grad_W=None, grad_gamma=None,
                  accumulate: bool = False, row_chunk: int = 0, workspace=None,
                  stream=None) -> dict:
         """Gradients of sum_t grad_logp[t] logp[t] (+ grad_entropy[t] entropy[t]) with respect
-        to the LM-head input ("grad_hidden", fp32 [T, H]) and W ("grad_W", fp32 [V, H]).
-        lse (and entropy) are the forward's outputs for these rows. grad_W may be given (fp32
-        [V, H]) to write into; with accumulate=True the chain continues from its contents."""
+        to the hidden rows ("grad_hidden", fp32 [T, H]; through the RMSNorm when the handle has
+        one), W ("grad_W", fp32 [V, H]) and the RMSNorm's gamma ("grad_gamma", fp32 [H]).
+        lse (and entropy) are the forward's outputs for these rows. grad_W / grad_gamma may be
+        given to write into; with accumulate=True their chains continue from their contents."""
         import torch
 
         bf = (torch.bfloat16, torch.int16, torch.uint16)
@@ -254,6 +256,9 @@ class Logprob:
                 raise ValueError("grad_entropy needs the forward's entropy")
         if entropy is not None:
             self._check(entropy, (torch.float32,), "entropy", (T,))
+        self._gamma(gamma)
+        if want_gamma is None:
+            want_gamma = self.rmsnorm
         dev = torch.device("cuda", self.device)
         need = rlk_logprob_backward_workspace_size(self.config, T, row_chunk)
         if workspace is not None:
@@ -271,11 +276,19 @@ class Logprob:
             else:
                 self._check(grad_W, (torch.float32,), "grad_W", (V, H))
             out["grad_W"] = grad_W
+        if want_gamma:
+            if grad_gamma is None:
+                if accumulate:
+                    raise ValueError("accumulate=True needs grad_gamma")
+                grad_gamma = torch.empty((H,), dtype=torch.float32, device=dev)
+            else:
+                self._check(grad_gamma, (torch.float32,), "grad_gamma", (H,))
+            out["grad_gamma"] = grad_gamma
         s = stream if stream is not None else torch.cuda.current_stream(dev)
         rlk_logprob_backward(self.handle, hidden.data_ptr(), W.data_ptr(), targets.data_ptr(), T,
-                             None, lse.data_ptr(), _ptr(entropy), grad_logp.data_ptr(),
+                             _ptr(gamma), lse.data_ptr(), _ptr(entropy), grad_logp.data_ptr(),
                              _ptr(grad_entropy), _ptr(out.get("grad_hidden")),
-                             _ptr(out.get("grad_W")), None,
+                             _ptr(out.get("grad_W")), _ptr(out.get("grad_gamma")),
                              RLK_BWD_ACCUMULATE if accumulate else 0, row_chunk,
                              workspace.data_ptr(), workspace.numel(), s.cuda_stream)
         out["_workspace"] = workspace

@@ -20,6 +20,14 @@
 //  B3 dW[v, k] = one fp32 MFMA chain over the rows t ascending, 32 at a time, from +0 or from
 //     the stored dW (accumulate); rows are padded with zeros to a multiple of 128. Row chunks of
 //     a multiple of 128 rows continue the chain, so chunked and one-pass runs give the same bits.
+//     With the final RMSNorm, B1-B3 run on its bf16 output y (C12's bits, recomputed).
+//  B4 RMSNorm (optional). dy = B2's gradient w.r.t. y; the bf16 rounding of y is passed straight
+//     through. Per row: c = sum_k (dy_k gamma_k) x_k and ss = sum_k x_k^2, both in C12's order
+//     (lane l takes the 8-element groups l, l+64, .. sequentially, then the xor butterfly 32 ..
+//     1); r = RSQ(ss fl32(1/H) + eps) exactly as in C12; a = ((r r) r) fl32(1/H);
+//     dx_k = (dy_k gamma_k) r - x_k (c a). dgamma_k = a chain over groups of 128 rows ascending,
+//     from 0 or the stored dgamma, of P_q = sum over the group's rows ascending, from +0, of
+//     (dy_tk x_tk) r_t; row chunks of a multiple of 128 rows continue it.
 //
 // Layout of the backward's intermediates (all in the caller's workspace): dz [rows][S_c Lp] and
 // dzt [S_c Lp][rows padded] hold vocab index v = s L + c at the segment-padded position s Lp + c
@@ -312,6 +320,86 @@ __global__ void k_seg_tree(const float* part, int64_t stride, float* out, int64_
   }
 }
 
+__global__ void __launch_bounds__(256) k_rmsnorm_bwd(const RmsBwdArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.rows) return;
+  const uint16_t* __restrict__ x = a.x + (int64_t)row * a.H;
+  const float* __restrict__ dy = a.dy + (int64_t)row * a.H;
+  const int npieces = a.H / 8;
+  float ss = 0.0f, c = 0.0f;
+  for (int p = lane; p < npieces; p += 64) {
+    const u32x4 v = *(const u32x4*)(x + p * 8);
+    const u32x4 g = *(const u32x4*)(a.gamma + p * 8);
+    const f32x4 d0 = *(const f32x4*)(dy + p * 8);
+    const f32x4 d1 = *(const f32x4*)(dy + p * 8 + 4);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float xl = bf16_to_f32(v[w] & 0xffffu), xh = bf16_to_f32(v[w] >> 16);
+      const float gl = bf16_to_f32(g[w] & 0xffffu), gh = bf16_to_f32(g[w] >> 16);
+      const float dl = w < 2 ? d0[2 * w] : d1[2 * w - 4];
+      const float dh = w < 2 ? d0[2 * w + 1] : d1[2 * w - 3];
+      ss = ss + xl * xl;
+      ss = ss + xh * xh;
+      c = c + (dl * gl) * xl;
+      c = c + (dh * gh) * xh;
+    }
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    ss = ss + __shfl_xor(ss, d);
+    c = c + __shfl_xor(c, d);
+  }
+  const float v = ss * a.inv_H + a.eps;
+  const float r = a.portable ? p_rsq(v) : c_rsq(v);
+  const float b = c * (((r * r) * r) * a.inv_H);
+  if (a.r && lane == 0) a.r[row] = r;
+  if (!a.dx) return;
+  float* __restrict__ dx = a.dx + (int64_t)row * a.H;
+  for (int p = lane; p < npieces; p += 64) {
+    const u32x4 v8 = *(const u32x4*)(x + p * 8);
+    const u32x4 g = *(const u32x4*)(a.gamma + p * 8);
+    const f32x4 d0 = *(const f32x4*)(dy + p * 8);
+    const f32x4 d1 = *(const f32x4*)(dy + p * 8 + 4);
+    f32x4 o0, o1;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t wx = v8[e >> 1], wg = g[e >> 1];
+      const float xv = bf16_to_f32((e & 1) ? (wx >> 16) : (wx & 0xffffu));
+      const float gv = bf16_to_f32((e & 1) ? (wg >> 16) : (wg & 0xffffu));
+      const float dv = e < 4 ? d0[e] : d1[e - 4];
+      const float o = (dv * gv) * r - xv * b;
+      if (e < 4) o0[e] = o;
+      else o1[e - 4] = o;
+    }
+    *(f32x4*)(dx + p * 8) = o0;
+    *(f32x4*)(dx + p * 8 + 4) = o1;
+  }
+}
+
+__global__ void __launch_bounds__(256) k_dgamma_part(const float* dy, const uint16_t* x,
+                                                     const float* r, float* P, int rows, int H) {
+  const int k = blockIdx.x * 256 + threadIdx.x;
+  if (k >= H) return;
+  const int t0 = blockIdx.y * kGammaGroup;
+  const int t1 = min(rows, t0 + kGammaGroup);
+  float acc = 0.0f;
+  // the loads of 16 rows are issued ahead; the sum itself stays one sequential chain
+#pragma unroll 16
+  for (int t = t0; t < t1; ++t)
+    acc = acc + (dy[(int64_t)t * H + k] * bf16_to_f32(x[(int64_t)t * H + k])) * r[t];
+  P[(int64_t)blockIdx.y * H + k] = acc;
+}
+
+__global__ void __launch_bounds__(256) k_dgamma_chain(const float* P, int nq, int H,
+                                                      float* dgamma, int accumulate) {
+  const int k = blockIdx.x * 256 + threadIdx.x;
+  if (k >= H) return;
+  float acc = accumulate ? dgamma[k] : 0.0f;
+  for (int q = 0; q < nq; ++q) acc = acc + P[(int64_t)q * H + k];
+  dgamma[k] = acc;
+}
+
 template <class F>
 void with_bwd_modes(bool entg, bool temp, bool port, F&& f) {
   using T = std::true_type;
@@ -329,6 +417,27 @@ void with_bwd_modes(bool entg, bool temp, bool port, F&& f) {
 }
 
 }  // namespace
+
+hipError_t launch_rmsnorm_bwd(const RmsBwdArgs& a, hipStream_t s) {
+  if (a.rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_rmsnorm_bwd, dim3((unsigned)((a.rows + 3) / 4)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dgamma(const float* dy, const uint16_t* x, const float* r, float* P, int rows,
+                         int H, float* dgamma, bool accumulate, hipStream_t s) {
+  const int nq = (rows + kGammaGroup - 1) / kGammaGroup;
+  const unsigned cb = (unsigned)((H + 255) / 256);
+  if (nq > 0) {
+    hipLaunchKernelGGL(k_dgamma_part, dim3(cb, (unsigned)nq), dim3(256), 0, s, dy, x, r, P, rows,
+                       H);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k_dgamma_chain, dim3(cb), dim3(256), 0, s, P, nq, H, dgamma,
+                     accumulate ? 1 : 0);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm_dz(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;

@@ -620,9 +620,11 @@ namespace {
 struct BwdMap {
   int64_t L, Lp, J;    // segment length, padded length, padded vocab width S_c Lp
   int64_t chunk, Tp;   // rows per chunk, chunk rows padded to kBwdKPad
-  size_t wt, dz, dzt, ht, dpart, total;
+  size_t wt, dz, dzt, ht, dpart, y, dy, r, gp, total;
 };
 
+// want_h: a gradient w.r.t. the LM-head input is needed (grad_hidden, or grad_gamma through the
+// RMSNorm); want_w: grad_W.
 BwdMap bwd_map(const rlk_logprob_config_t& c, int64_t rows, int64_t row_chunk, bool want_h,
                bool want_w) {
   BwdMap m;
@@ -645,6 +647,12 @@ BwdMap bwd_map(const rlk_logprob_config_t& c, int64_t rows, int64_t row_chunk, b
   m.dzt = want_w ? take((size_t)m.J * (size_t)m.Tp * 2) : 0;
   m.ht = want_w ? take(H * (size_t)m.Tp * 2) : 0;
   m.dpart = (want_h && S > 1) ? take((size_t)S * (size_t)m.chunk * H * 4) : 0;
+  const bool rms = c.flags & RLK_FLAG_RMSNORM;
+  m.y = rms ? take((size_t)m.chunk * H * 2) : 0;
+  m.dy = (rms && want_h) ? take((size_t)m.chunk * H * 4) : 0;
+  m.r = (rms && want_h) ? take((size_t)m.chunk * 4) : 0;
+  m.gp = (rms && want_h) ? take((size_t)((m.chunk + rlk::kGammaGroup - 1) / rlk::kGammaGroup) * H * 4)
+                         : 0;
   m.total = std::max<size_t>(off, 256);
   return m;
 }
@@ -689,12 +697,15 @@ RLK_API rlk_status_t rlk_logprob_backward(rlk_logprob_t h, const void* hidden, c
   if (flags & ~RLK_BWD_ACCUMULATE) return fail(RLK_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", flags);
   rlk_status_t st = check_bwd_rows(c, num_rows, row_chunk);
   if (st != RLK_OK) return st;
-  if (c.flags & RLK_FLAG_RMSNORM)
-    return fail(RLK_ERR_UNSUPPORTED_SHAPE, "the backward through the final RMSNorm is not built");
-  if (rms_gamma || grad_gamma)
+  const bool rms = c.flags & RLK_FLAG_RMSNORM;
+  if (!rms && (rms_gamma || grad_gamma))
     return fail(RLK_ERR_CONTRACT, "rms_gamma / grad_gamma given but RLK_FLAG_RMSNORM not set");
-  const bool want_h = grad_hidden != nullptr, want_w = grad_W != nullptr;
-  if (!want_h && !want_w) return fail(RLK_ERR_INVALID_ARGUMENT, "no gradient requested");
+  if (rms && num_rows > 0 && !rms_gamma)
+    return fail(RLK_ERR_INVALID_ARGUMENT, "rms_gamma is required with RLK_FLAG_RMSNORM");
+  const bool want_x = grad_hidden != nullptr, want_w = grad_W != nullptr;
+  const bool want_g = grad_gamma != nullptr;
+  const bool want_h = want_x || want_g;  // a gradient w.r.t. the LM-head input is needed
+  if (!want_x && !want_w && !want_g) return fail(RLK_ERR_INVALID_ARGUMENT, "no gradient requested");
   if (grad_entropy && !(c.flags & RLK_FLAG_ENTROPY))
     return fail(RLK_ERR_CONTRACT, "grad_entropy given but RLK_FLAG_ENTROPY not set");
   if (grad_entropy && !entropy)
@@ -704,7 +715,8 @@ RLK_API rlk_status_t rlk_logprob_backward(rlk_logprob_t h, const void* hidden, c
   if (!W_lm && want_w) return fail(RLK_ERR_INVALID_ARGUMENT, "W is required");
   if (!aligned16(hidden) || !aligned16(W_lm) || !aligned16(targets) || !aligned16(lse) ||
       !aligned16(grad_logp) || !aligned16(entropy) || !aligned16(grad_entropy) ||
-      !aligned16(grad_hidden) || !aligned16(grad_W) || !aligned16(workspace))
+      !aligned16(grad_hidden) || !aligned16(grad_W) || !aligned16(workspace) ||
+      !aligned16(rms_gamma) || !aligned16(grad_gamma))
     return fail(RLK_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
   const BwdMap m = bwd_map(c, num_rows, row_chunk, want_h, want_w);
   if (!workspace || workspace_bytes < m.total)
@@ -724,6 +736,10 @@ RLK_API rlk_status_t rlk_logprob_backward(rlk_logprob_t h, const void* hidden, c
       e = rlk::launch_zero_f32(grad_W, V * H, s);
       if (e != hipSuccess) return hip_fail(e, "zero launch");
     }
+    if (want_g && !accumulate) {
+      e = rlk::launch_zero_f32(grad_gamma, H, s);
+      if (e != hipSuccess) return hip_fail(e, "zero launch");
+    }
     return ok();
   }
   uint16_t* WT = reinterpret_cast<uint16_t*>(ws + m.wt);
@@ -731,6 +747,11 @@ RLK_API rlk_status_t rlk_logprob_backward(rlk_logprob_t h, const void* hidden, c
   uint16_t* dzt = reinterpret_cast<uint16_t*>(ws + m.dzt);
   uint16_t* hT = reinterpret_cast<uint16_t*>(ws + m.ht);
   float* dpart = reinterpret_cast<float*>(ws + m.dpart);
+  uint16_t* ynorm = reinterpret_cast<uint16_t*>(ws + m.y);
+  float* dy = reinterpret_cast<float*>(ws + m.dy);
+  float* rrow = reinterpret_cast<float*>(ws + m.r);
+  float* gpart = reinterpret_cast<float*>(ws + m.gp);
+  const uint16_t* gam = static_cast<const uint16_t*>(rms_gamma);
   const uint16_t* hid = static_cast<const uint16_t*>(hidden);
   const uint16_t* Wb = static_cast<const uint16_t*>(W_lm);
   if (want_h) {
@@ -752,11 +773,27 @@ RLK_API rlk_status_t rlk_logprob_backward(rlk_logprob_t h, const void* hidden, c
     const int64_t r1 = std::min<int64_t>(num_rows, r0 + m.chunk);
     const int64_t n = r1 - r0;
     const int64_t np = (int64_t)round_up((size_t)n, rlk::kBwdKPad);
+    // the LM-head input of these rows: the hidden rows, or their RMSNorm (C12, recomputed)
+    const uint16_t* hin = hid + r0 * H;
+    if (rms) {
+      rlk::RmsArgs ra;
+      ra.x = hin;
+      ra.gamma = gam;
+      ra.y = ynorm;
+      ra.rows = (int32_t)n;
+      ra.H = H;
+      ra.inv_H = 1.0f / (float)H;
+      ra.eps = c.rms_eps;
+      ra.portable = (c.flags & RLK_FLAG_PORTABLE_EXP) ? 1 : 0;
+      e = rlk::launch_rmsnorm(ra, s);
+      if (e != hipSuccess) return hip_fail(e, "rmsnorm launch");
+      hin = ynorm;
+    }
     // B1: dz and its transpose
     rlk::GemmArgs a{};
     a.A = Wb;
     a.lda = H;
-    a.B = hid + r0 * H;
+    a.B = hin;
     a.ldb = H;
     a.M = (int32_t)V;
     a.N = (int32_t)n;
@@ -799,20 +836,42 @@ RLK_API rlk_status_t rlk_logprob_backward(rlk_logprob_t h, const void* hidden, c
       g.M = H;
       g.N = (int32_t)n;
       g.K = (int32_t)m.Lp;
-      g.C = S > 1 ? dpart : grad_hidden + r0 * H;
+      float* dh = rms ? dy : grad_hidden + r0 * H;
+      g.C = S > 1 ? dpart : dh;
       g.ldc = H;
       g.c_batch = n * H;
       e = rlk::launch_gemm_out(g, S, s);
       if (e != hipSuccess) return hip_fail(e, "dh launch");
       if (S > 1) {
-        e = rlk::launch_seg_tree(dpart, n * H, S, grad_hidden + r0 * H, n * H, s);
+        e = rlk::launch_seg_tree(dpart, n * H, S, dh, n * H, s);
         if (e != hipSuccess) return hip_fail(e, "dh tree launch");
+      }
+      if (rms) {
+        // B4: through the RMSNorm to its input, and the gamma gradient
+        rlk::RmsBwdArgs rb;
+        rb.x = hid + r0 * H;
+        rb.gamma = gam;
+        rb.dy = dy;
+        rb.dx = want_x ? grad_hidden + r0 * H : nullptr;
+        rb.r = rrow;
+        rb.rows = (int32_t)n;
+        rb.H = H;
+        rb.inv_H = 1.0f / (float)H;
+        rb.eps = c.rms_eps;
+        rb.portable = (c.flags & RLK_FLAG_PORTABLE_EXP) ? 1 : 0;
+        e = rlk::launch_rmsnorm_bwd(rb, s);
+        if (e != hipSuccess) return hip_fail(e, "rmsnorm backward launch");
+        if (want_g) {
+          e = rlk::launch_dgamma(dy, hid + r0 * H, rrow, gpart, (int)n, H, grad_gamma,
+                                 accumulate || chunk_no > 0, s);
+          if (e != hipSuccess) return hip_fail(e, "dgamma launch");
+        }
       }
     }
     if (want_w) {
       // B3: the chain over rows continues from the previous chunk
       rlk::TransposeArgs ta;
-      ta.in = hid + r0 * H;
+      ta.in = hin;
       ta.ldi = H;
       ta.R = n;
       ta.C = H;

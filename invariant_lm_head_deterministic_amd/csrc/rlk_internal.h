@@ -139,6 +139,27 @@ struct TransposeArgs {
   int64_t L, Lp;
 };
 
+// B4: the final RMSNorm's backward, one wave per row. dx (optional) and r (optional) per row.
+struct RmsBwdArgs {
+  const uint16_t* x;        // bf16 [rows, H] (the RMSNorm's input)
+  const uint16_t* gamma;    // bf16 [H]
+  const float* dy;          // fp32 [rows, H]: gradient w.r.t. the RMSNorm's output
+  float* dx;                // fp32 [rows, H] or null
+  float* r;                 // fp32 [rows] or null: the rows' 1/rms (C12 bits)
+  int32_t rows;
+  int32_t H;
+  float inv_H;
+  float eps;
+  int32_t portable;
+};
+constexpr int kGammaGroup = 128;  // rows per sequential group of the dgamma sum (B4)
+
+hipError_t launch_rmsnorm_bwd(const RmsBwdArgs& a, hipStream_t s);
+// P[q][k] = sum over rows t of group q (kGammaGroup rows, ascending, from +0) of
+// (dy[t][k] x[t][k]) r[t]; then dgamma[k] = chain over q ascending from 0 or dgamma[k].
+hipError_t launch_dgamma(const float* dy, const uint16_t* x, const float* r, float* P, int rows,
+                         int H, float* dgamma, bool accumulate, hipStream_t s);
+
 hipError_t launch_gemm_dz(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_out(const GemmArgs& a, int batches, hipStream_t s);
 hipError_t launch_transpose(const TransposeArgs& a, hipStream_t s);

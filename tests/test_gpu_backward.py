@@ -154,7 +154,7 @@ def test_backward_refusals(rlk):
     lse = torch.zeros(8, dtype=torch.float32, device="cuda")
     gd = torch.from_numpy(g).cuda()
     lp = rlk.Logprob(H, V, rmsnorm=True)
-    with pytest.raises(rlk.RlkError):
+    with pytest.raises(rlk.RlkError):  # the RMSNorm's gamma is required
         lp.backward(hd, Wd, yd, lse, gd)
     lp = rlk.Logprob(H, V)  # no entropy flag
     with pytest.raises(rlk.RlkError):
@@ -177,3 +177,121 @@ def test_backward_full_size_sampled(rlk):
     rows_h = np.array([0, 1, 777, 2048, 4095])
     rows_w = np.concatenate([y[[0, 777]], [0, 37983, 37984, 75968, 151935]])
     _check(got, h, W, y, g, None, 1.0, rows_h=rows_h, rows_w=rows_w)
+
+
+def _rms_inputs(T, H, V, cfg, pad_every=0):
+    x = datagen.normal_bf16(T, H, cfg, datagen.TID_HIDDEN)
+    W = datagen.normal_bf16(V, H, cfg, datagen.TID_W, scale=0.02)
+    gam = datagen.normal_bf16(1, H, cfg, datagen.TID_GAMMA, scale=0.1, mean=1.0)[0]
+    y = datagen.uniform_targets(T, V, cfg)
+    if pad_every:
+        y[::pad_every] = -1
+    g = np.random.default_rng(cfg).normal(size=T).astype(np.float32)
+    gH = np.random.default_rng(cfg + 1).normal(size=T).astype(np.float32)
+    return x, W, gam, y, g, gH
+
+
+def _run_rms(rlk, x, W, gam, y, g, gH, *, S, tau, eps=1e-6, **kw):
+    import torch
+
+    T, H = x.shape
+    V = W.shape[0]
+    lp = rlk.Logprob(H, V, vocab_segments=S, temperature=tau, rmsnorm=True, rms_eps=eps,
+                     entropy=gH is not None)
+    xd, Wd, yd, gd_ = dev_bits(x), dev_bits(W), dev_i32(y), dev_bits(gam)
+    fw = lp.forward(xd, Wd, yd, gamma=gd_)
+    gd = torch.from_numpy(g).cuda()
+    gHd = None if gH is None else torch.from_numpy(gH).cuda()
+    out = lp.backward(xd, Wd, yd, fw["lse"], gd, entropy=fw.get("entropy"), grad_entropy=gHd,
+                      gamma=gd_, **kw)
+    torch.cuda.synchronize()
+    return {k: host(v) for k, v in out.items() if not k.startswith("_")}, (lp, xd, Wd, yd, gd_, fw,
+                                                                            gd, gHd)
+
+
+def _rel(got, ref):
+    d = np.abs(got.astype(np.float64) - ref)
+    return float(d.max() / max(np.abs(ref).max(), 1e-300)), \
+        float(np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-300))
+
+
+@pytest.mark.parametrize("T,H,V,S,tau,ent", [
+    (200, 256, 3000, 4, 0.7, True),
+    (90, 384, 2000, 2, 1.0, False),
+])
+def test_backward_rmsnorm_matches_oracle(rlk, T, H, V, S, tau, ent):
+    """Through the RMSNorm, on top of the dz flips of the plain backward, the bf16 rounding of y
+    may land one step apart in the fp32 and fp64 RMSNorms (rarely), and r is an fp32 reciprocal
+    square root (~1e-7 relative). grad_W = dz^T y then moves by at most one bf16 step of dz or of
+    y per term: |err| <= 2^-6 (|dz|^T @ |y|) per element. grad_hidden and grad_gamma mix every
+    element of a row, so their bar is relative: max error <= 1e-3 of the largest element and a
+    relative Frobenius error <= 1e-4."""
+    x, W, gam, y, g, gH = _rms_inputs(T, H, V, 600 + T, 7)
+    gH = gH if ent else None
+    say(f"backward rmsnorm T={T} H={H} V={V} S={S} tau={tau} ent={ent}")
+    got, _ = _run_rms(rlk, x, W, gam, y, g, gH, S=S, tau=tau)
+    want = oracle.grads(x, W, y, g, gH, tau=tau, gamma_bits=gam, rms_eps=1e-6)
+    for key, ref in (("grad_hidden", want["dh"]), ("grad_gamma", want["dgamma"])):
+        mx, fro = _rel(got[key], ref)
+        print(key, "max/maxref", mx, "fro", fro, flush=True)
+        assert mx <= 1e-3 and fro <= 1e-4, (key, mx, fro)
+    yn = oracle.rmsnorm_bf16(oracle.bf16_bits_to_f64(x), oracle.bf16_bits_to_f64(gam), 1e-6)
+    dz = np.abs(oracle.dlogits(yn @ oracle.bf16_bits_to_f64(W).T / tau, y, g, gH, tau))
+    lim = 2.0 ** -6 * (dz.T @ np.abs(yn)) + 1e-30
+    d = np.abs(got["grad_W"].astype(np.float64) - want["dW"])
+    print("grad_W max/lim", float((d / lim).max()), "fro", _rel(got["grad_W"], want["dW"])[1],
+          flush=True)
+    assert np.all(d <= lim)
+    assert _rel(got["grad_W"], want["dW"])[1] <= 1e-3
+
+
+def test_backward_rmsnorm_chunks_and_accumulation_bitwise(rlk):
+    import torch
+
+    T, H, V = 300, 256, 2500
+    x, W, gam, y, g, gH = _rms_inputs(T, H, V, 610, 13)
+    say("backward rmsnorm invariances")
+    one, (lp, xd, Wd, yd, gd_, fw, gd, gHd) = _run_rms(rlk, x, W, gam, y, g, gH, S=4, tau=1.0)
+    ent = fw["entropy"]
+    o = lp.backward(xd, Wd, yd, fw["lse"], gd, entropy=ent, grad_entropy=gHd, gamma=gd_,
+                    row_chunk=128)
+    torch.cuda.synchronize()
+    for k in ("grad_hidden", "grad_W", "grad_gamma"):
+        assert_bitwise(o[k], one[k], f"{k} chunk 128")
+    gw = torch.empty((V, H), dtype=torch.float32, device="cuda")
+    gg = torch.empty((H,), dtype=torch.float32, device="cuda")
+    sl = [slice(0, 256), slice(256, T)]
+    for i, s_ in enumerate(sl):
+        lp.backward(xd[s_].contiguous(), Wd, yd[s_].contiguous(), fw["lse"][s_].contiguous(),
+                    gd[s_].contiguous(), entropy=ent[s_].contiguous(),
+                    grad_entropy=gHd[s_].contiguous(), gamma=gd_, want_hidden=False, grad_W=gw,
+                    grad_gamma=gg, accumulate=i > 0)
+    torch.cuda.synchronize()
+    assert_bitwise(gw, one["grad_W"], "dW accumulated")
+    assert_bitwise(gg, one["grad_gamma"], "dgamma accumulated")
+
+
+def test_backward_norm_head_rows_full_width(rlk):
+    """norm_head's widths (H=5120, V=151936, tau=0.7, entropy) on its first 512 rows."""
+    w = datagen.WORKLOADS["norm_head"]
+    T = 512
+    x = datagen.hidden_bits(w, rows=T)
+    W = datagen.weight_bits(w)
+    gam = datagen.gamma_bits(w)
+    y = np.load("tests/golden/targets_norm_head.npy")[:T].astype(np.int32)
+    g = np.random.default_rng(620).normal(size=T).astype(np.float32)
+    gH = np.random.default_rng(621).normal(size=T).astype(np.float32)
+    say("backward norm_head 512 rows")
+    got, _ = _run_rms(rlk, x, W, gam, y, g, gH, S=w.segments, tau=w.tau, eps=w.rms_eps)
+    want = oracle.grads(x, W, y, g, gH, tau=w.tau, gamma_bits=gam, rms_eps=w.rms_eps,
+                        dW_rows=np.concatenate([y[:3], [0, 151935]]))
+    mx, fro = _rel(got["grad_hidden"], want["dh"])
+    print("grad_hidden", mx, fro, flush=True)
+    assert mx <= 1e-3 and fro <= 1e-4
+    mx, fro = _rel(got["grad_gamma"], want["dgamma"])
+    print("grad_gamma", mx, fro, flush=True)
+    assert mx <= 1e-3 and fro <= 1e-4
+    rw = np.concatenate([y[:3], [0, 151935]])
+    mx, fro = _rel(got["grad_W"][rw], want["dW"])
+    print("grad_W", mx, fro, flush=True)
+    assert mx <= 1e-3 and fro <= 1e-4
