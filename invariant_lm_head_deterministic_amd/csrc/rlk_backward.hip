@@ -31,9 +31,10 @@
 //
 // Layout of the backward's intermediates (all in the caller's workspace): dz [rows][S_c Lp] and
 // dzt [S_c Lp][rows padded] hold vocab index v = s L + c at the segment-padded position s Lp + c
-// (L = V / S_c, Lp = L rounded up to 128); WT [H][S_c Lp] and hT [H][rows padded] are the
-// transposed operands, so every GEMM here is an NT GEMM with K contiguous in both operands, the
-// shape of the forward's K loop (nt_mainloop).
+// (L = V / S_c, Lp = L rounded up to 128), with zeros at the padding positions and padding rows;
+// WT [H][S_c Lp] and hT [H][rows padded] are the transposed operands (zeros in their padding), so
+// every GEMM here is an NT GEMM with K contiguous in both operands, the shape of the forward's K
+// loop (nt_mainloop). The dz kernel runs over the padded positions, so it writes those zeros.
 
 #include <algorithm>
 #include <utility>
@@ -99,29 +100,42 @@ int64_t gemm_blocks(int M, int N) {
   return (n + 7) / 8 * 8;
 }
 
-// segment-padded position of vocab index v, and back (-1 for a padding position)
-__device__ __forceinline__ int64_t pad_col(int64_t v, int64_t L, int64_t Lp) {
-  const int64_t s = v / L;
-  return v + s * (Lp - L);
-}
-__device__ __forceinline__ int64_t unpad_row(int64_t n, int64_t L, int64_t Lp) {
-  const int64_t s = n / Lp;
-  const int64_t c = n - s * Lp;
-  return c < L ? s * L + c : -1;
+// Output row of this lane's B row in B block j of the wave (OUT epilogue), or null for a row past
+// the tile or a padding row of the segment-padded vocab layout. 32-bit index math: B rows are
+// below 2^31.
+__device__ __forceinline__ const float* out_row(const GemmArgs& a, const float* C, const GTile& t,
+                                                int wt, int j, int lane) {
+  const int nn = 16 * (wt * kGNB16 + j) + (lane & 15);
+  if (nn >= t.nrows) return nullptr;
+  const uint32_t n = (uint32_t)(t.n0 + nn);
+  uint32_t row = n;
+  if (a.map_rows) {
+    const uint32_t Lp = (uint32_t)a.seg_pad, L = (uint32_t)a.seg_len;
+    const uint32_t sg = n / Lp;
+    const uint32_t c = n - sg * Lp;
+    if (c >= L) return nullptr;
+    row = sg * L + c;
+  }
+  return C + (int64_t)row * a.ldc;
 }
 
 // One B1 value.
 template <bool ENTG, bool TEMP, bool PORT>
-__device__ __forceinline__ uint16_t dz_one(float acc, int64_t v, int y, float g, float l, float gh,
+__device__ __forceinline__ uint16_t dz_one(float acc, int v, int y, float g, float l, float gh,
                                            float e, float inv_tau) {
-  if (y < 0) return 0;
   const float zp = TEMP ? acc * inv_tau : acc;
   const float p = EXP<PORT>(zp - l);
-  const float d = (v == (int64_t)y) ? 1.0f - p : -p;
+  const float d = (v == y) ? 1.0f - p : -p;
   float q = g * d;
   if constexpr (ENTG) q = q - gh * (p * ((zp - l) + e));
   if constexpr (TEMP) q = q * inv_tau;
-  return bf16_rne(q);
+  // bf16_rne (NaN kept quiet) and the padded-row zero as mask arithmetic: the compiler would
+  // otherwise wrap each element in branches
+  const uint32_t u = __float_as_uint(q);
+  const uint32_t rne = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t nan = 0u - (uint32_t)((u & 0x7fffffffu) > 0x7f800000u);
+  const uint32_t bits = (rne & ~nan) | (((u >> 16) | 0x40u) & nan);
+  return (uint16_t)(bits & (0u - (uint32_t)(y >= 0)));
 }
 
 // The backward's NT GEMM tile kernel (see GemmArgs). EPI 0 = DZ, 1 = OUT.
@@ -140,16 +154,41 @@ __global__ void __launch_bounds__(64 * kGWaves) k_gemm(const GemmArgs a) {
   const int wv = wave % kGVW;
   const int wt = wave / kGVW;
   const int64_t yb = blockIdx.y;
-  const uint16_t* __restrict__ At = a.A + yb * a.a_batch + (int64_t)t.m0 * a.lda;
   const uint16_t* __restrict__ Bt = a.B + yb * a.b_batch + (int64_t)t.n0 * a.ldb;
 
-  // staging offsets as in the forward: rows past the tile are clamped to its last row
+  // Staging offsets as in the forward: rows past the tile are clamped to its last row. DZ runs
+  // over the segment-padded vocab positions: tile row m reads W row v(m), a padding position
+  // the last row of its segment (its result is replaced by 0). v(m) never decreases, and the
+  // tile's real rows are consecutive in W, so one descriptor from v(first) covers them.
   uint32_t ago[kGWI], bgo[kGHI];
+  const uint16_t* __restrict__ At;
+  int64_t a_rows;  // rows the A descriptor spans
+  if constexpr (EPI == 0) {
+    const uint32_t L = (uint32_t)a.seg_len, Lp = (uint32_t)a.seg_pad;
+    auto vrow = [&](uint32_t m) {
+      const uint32_t sg = m / Lp;
+      return sg * L + min(m - sg * Lp, L - 1);
+    };
+    const uint32_t vf = (uint32_t)uni((int)vrow((uint32_t)t.m0));
+    const uint32_t vl = (uint32_t)uni((int)vrow((uint32_t)(t.m0 + t.mrows - 1)));
+    At = a.A + (int64_t)vf * a.lda;
+    a_rows = (int64_t)(vl - vf) + 1;
 #pragma unroll
-  for (int q = 0; q < kGWI; ++q) {
-    const int r = 8 * (q * kGWaves + wave) + (lane >> 3);
-    const int c = (lane & 7) ^ swz(r);
-    ago[q] = (uint32_t)(((int64_t)min(r, t.mrows - 1) * a.lda + c * 8) * 2);
+    for (int q = 0; q < kGWI; ++q) {
+      const int r = 8 * (q * kGWaves + wave) + (lane >> 3);
+      const int c = (lane & 7) ^ swz(r);
+      const uint32_t v = vrow((uint32_t)(t.m0 + min(r, t.mrows - 1))) - vf;
+      ago[q] = (uint32_t)(((int64_t)v * a.lda + c * 8) * 2);
+    }
+  } else {
+    At = a.A + yb * a.a_batch + (int64_t)t.m0 * a.lda;
+    a_rows = t.mrows;
+#pragma unroll
+    for (int q = 0; q < kGWI; ++q) {
+      const int r = 8 * (q * kGWaves + wave) + (lane >> 3);
+      const int c = (lane & 7) ^ swz(r);
+      ago[q] = (uint32_t)(((int64_t)min(r, t.mrows - 1) * a.lda + c * 8) * 2);
+    }
   }
 #pragma unroll
   for (int q = 0; q < kGHI; ++q) {
@@ -157,8 +196,7 @@ __global__ void __launch_bounds__(64 * kGWaves) k_gemm(const GemmArgs a) {
     const int c = (lane & 7) ^ swz(r);
     bgo[q] = (uint32_t)(((int64_t)min(r, t.nrows - 1) * a.ldb + c * 8) * 2);
   }
-  const __amdgpu_buffer_rsrc_t ra =
-      make_rsrc(At, (int)(((int64_t)(t.mrows - 1) * a.lda + a.K) * 2));
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(At, (int)(((a_rows - 1) * a.lda + a.K) * 2));
   const __amdgpu_buffer_rsrc_t rb =
       make_rsrc(Bt, (int)(((int64_t)(t.nrows - 1) * a.ldb + a.K) * 2));
 
@@ -167,17 +205,21 @@ __global__ void __launch_bounds__(64 * kGWaves) k_gemm(const GemmArgs a) {
 #pragma unroll
   for (int i = 0; i < kGVB16; ++i)
 #pragma unroll
-    for (int j = 0; j < kGNB16; ++j) {
+    for (int j = 0; j < kGNB16; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0f;
-      if constexpr (EPI == 1 && ACC) {
-        const int m = t.m0 + 16 * (wv * kGVB16 + i) + 4 * (lane >> 4);
-        const int nn = 16 * (wt * kGNB16 + j) + (lane & 15);
-        const int64_t n = t.n0 + nn;
-        const int64_t row = a.map_rows ? unpad_row(n, a.seg_len, a.seg_pad) : n;
-        if (nn < t.nrows && m < a.M && row >= 0) acc[i][j] = *(const f32x4*)(C + row * a.ldc + m);
-      }
-    }
+  if constexpr (EPI == 1 && ACC) {
+    static_for<kGNB16>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      const float* crow = out_row(a, C, t, wt, j, lane);
+      if (!crow) return;
+      const int mb = t.m0 + 16 * wv * kGVB16 + 4 * (lane >> 4);
+      static_for<kGVB16>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        if (mb + 16 * i < a.M) acc[i][j] = *(const f32x4*)(crow + mb + 16 * i);
+      });
+    });
+  }
   nt_mainloop<kGWaves, kGVB16, kGNB16, kGWI, kGHI>(acc, lds_a0, lds_a1, lds_b0, lds_b1, ra, rb,
                                                    ago, bgo, a.K / kKStage, wave, lane, wv, wt);
 
@@ -186,15 +228,15 @@ __global__ void __launch_bounds__(64 * kGWaves) k_gemm(const GemmArgs a) {
   // computed before the K loop stays live across it.
   const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   if constexpr (EPI == 1) {
-    static_for<kGVB16>([&](auto ic) {
-      constexpr int i = decltype(ic)::value;
-      static_for<kGNB16>([&](auto jc) {
-        constexpr int j = decltype(jc)::value;
-        const int m = t.m0 + 16 * (wv * kGVB16 + i) + 4 * (ln >> 4);
-        const int nn = 16 * (wt * kGNB16 + j) + (ln & 15);
-        const int64_t n = t.n0 + nn;
-        const int64_t row = a.map_rows ? unpad_row(n, a.seg_len, a.seg_pad) : n;
-        if (nn < t.nrows && m < a.M && row >= 0) *(f32x4*)(C + row * a.ldc + m) = acc[i][j];
+    // one output row pointer per B block (row(n) needs one division), then constant offsets
+    static_for<kGNB16>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      float* crow = const_cast<float*>(out_row(a, C, t, wt, j, ln));
+      if (!crow) return;
+      const int mb = t.m0 + 16 * wv * kGVB16 + 4 * (ln >> 4);
+      static_for<kGVB16>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        if (mb + 16 * i < a.M) *(f32x4*)(crow + mb + 16 * i) = acc[i][j];
       });
     });
   } else {
@@ -213,43 +255,61 @@ __global__ void __launch_bounds__(64 * kGWaves) k_gemm(const GemmArgs a) {
       hj[j] = ENTG ? a.gH[n] : 0.0f;
       ej[j] = ENTG ? a.ent[n] : 0.0f;
     }
-    const bool fast = (a.seg_len & 3) == 0;
+    const int q = ln & 3;
+    const bool lo2 = q < 2;
+    // v_perm_b32 selectors of the quad transpose (bytes 0-3 from the second operand, 4-7 from
+    // the first): odd q takes the low halves, even q the high halves
+    const uint32_t ps2 = (q & 1) ? 0x05040100u : 0x07060302u;
+    const uint32_t pu0 = (q & 1) ? 0x03020504u : 0x05040100u;
+    const uint32_t pu1 = (q & 1) ? 0x03020706u : 0x07060100u;
+    // hoisted addressing: the lane's dz row for B block 0 (block j adds 16 rows) and the quad's
+    // first dzt column; positions, segments and vocab indices in 32-bit math (< 2^31)
+    const int64_t tl = t.n0 + 16 * wt * kGNB16 + (ln & 15);
+    const int64_t tq = t.n0 + 16 * wt * kGNB16 + (ln & 12);
+    uint16_t* const dzr = a.dz ? a.dz + tl * a.lddz : nullptr;
+    const int64_t dz_j = 16 * a.lddz;
+    const uint32_t L = (uint32_t)a.seg_len, Lp = (uint32_t)a.seg_pad;
+    const uint32_t cb = (uint32_t)(t.m0 + 16 * wv * kGVB16 + 4 * (ln >> 4));
     static_for<kGVB16>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
-      const int64_t v0 = t.m0 + 16 * (wv * kGVB16 + i) + 4 * (ln >> 4);
-      if (v0 >= a.V) return;
-      const int64_t s0 = v0 / a.seg_len;
-      const int64_t col0 = v0 + s0 * (a.seg_pad - a.seg_len);
+      // 4 consecutive padded positions col0 .. col0+3 (one segment: Lp is a multiple of 128)
+      const uint32_t col0 = cb + 16 * i;
+      const uint32_t sg = col0 / Lp;
+      const uint32_t c0 = col0 - sg * Lp;  // position inside the segment
+      const int v0 = (int)(sg * L + c0);   // vocab index of col0 when c0 < L
+      uint16_t* const dztr = a.dzt ? a.dzt + (int64_t)(col0 + q) * a.lddzt + tq : nullptr;
+      const bool col_ok = (int)col0 < a.M;
       static_for<kGNB16>([&](auto jc) {
         constexpr int j = decltype(jc)::value;
         const int nn = 16 * (wt * kGNB16 + j) + (ln & 15);
-        if (nn >= t.nrows) return;
-        const int64_t n = t.n0 + nn;
+        // every lane computes (rows past the tile have y = -1, padding positions give 0), so
+        // the quad exchange below runs with all lanes active
         uint16_t b[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          b[r] = dz_one<ENTG, TEMP, PORT>(acc[i][j][r], v0 + r, yj[j], gj[j], lj[j], hj[j], ej[j],
-                                          a.inv_tau);
-        if (fast && v0 + 3 < a.V) {
-          // the 4 indices share a segment: contiguous, 8-byte aligned positions
-          if (a.dz) {
-            const uint32_t lo = (uint32_t)b[0] | ((uint32_t)b[1] << 16);
-            const uint32_t hi = (uint32_t)b[2] | ((uint32_t)b[3] << 16);
-            *(uint2*)(a.dz + n * a.lddz + col0) = make_uint2(lo, hi);
-          }
-          if (a.dzt) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) a.dzt[(col0 + r) * a.lddzt + n] = b[r];
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int64_t v = v0 + r;
-            if (v >= a.V) continue;
-            const int64_t col = pad_col(v, a.seg_len, a.seg_pad);
-            if (a.dz) a.dz[n * a.lddz + col] = b[r];
-            if (a.dzt) a.dzt[col * a.lddzt + n] = b[r];
-          }
+        for (int r = 0; r < 4; ++r) {
+          const uint16_t x = dz_one<ENTG, TEMP, PORT>(acc[i][j][r], v0 + r, yj[j], gj[j], lj[j],
+                                                      hj[j], ej[j], a.inv_tau);
+          b[r] = c0 + r < L ? x : (uint16_t)0;
+        }
+        const uint32_t w0 = (uint32_t)b[0] | ((uint32_t)b[1] << 16);
+        const uint32_t w1 = (uint32_t)b[2] | ((uint32_t)b[3] << 16);
+        if (dzr && nn < t.nrows && col_ok) *(uint2*)(dzr + j * dz_j + col0) = make_uint2(w0, w1);
+        if (dztr) {
+          // A quad (lanes 4k .. 4k+3) holds the 4 x 4 block dz[col0 + r][t0 + lane & 3]; two
+          // exchanges transpose it, so lane q ends with dz[col0 + q][t0 .. t0+3] for one 8-byte
+          // store. Step 1 swaps row pairs across q ^ 2, step 2 single elements across q ^ 1.
+          const uint32_t k1 = lo2 ? w0 : w1;
+          const uint32_t s1 = lo2 ? w1 : w0;
+          const uint32_t r1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)s1, 0x4E, 0xf, 0xf, false);
+          const uint32_t A = lo2 ? k1 : r1;  // rows R, R+1 at column q & 1
+          const uint32_t B = lo2 ? r1 : k1;  // rows R, R+1 at column (q & 1) + 2
+          // odd q sends (A.lo, B.lo), even q (A.hi, B.hi); then each keeps its own half and
+          // places the received one (byte selects of v_perm_b32, per-lane selectors)
+          const uint32_t s2 = __builtin_amdgcn_perm(B, A, ps2);
+          const uint32_t r2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)s2, 0xB1, 0xf, 0xf, false);
+          const uint32_t u0 = __builtin_amdgcn_perm(r2, A, pu0);
+          const uint32_t u1 = __builtin_amdgcn_perm(r2, B, pu1);
+          if (col_ok && tq + 16 * j < a.lddzt) *(uint2*)(dztr + 16 * j) = make_uint2(u0, u1);
         }
       });
     });
@@ -281,17 +341,6 @@ __global__ void __launch_bounds__(256) k_transpose(const TransposeArgs a) {
     const int64_t j = j0 + pj * 8;
     if (j >= a.J) continue;
     *(u32x4*)(a.out + (c0 + cr) * a.ldo + j) = *(const u32x4*)(&tile[cr][pj * 8]);
-  }
-}
-
-__global__ void k_zero_rect(uint16_t* p, int64_t ld, int64_t r0, int64_t r1, int64_t c0,
-                            int64_t c1) {
-  const int64_t w = c1 - c0;
-  const int64_t n = (r1 - r0) * w;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t r = r0 + i / w, c = c0 + i % w;
-    p[r * ld + c] = 0;
   }
 }
 
@@ -467,15 +516,6 @@ hipError_t launch_transpose(const TransposeArgs& a, hipStream_t s) {
   if (a.J <= 0 || a.C <= 0) return hipSuccess;
   const dim3 grid((unsigned)((a.J + 63) / 64), (unsigned)((a.C + 63) / 64));
   hipLaunchKernelGGL(k_transpose, grid, dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_zero_rect(uint16_t* p, int64_t ld, int64_t r0, int64_t r1, int64_t c0,
-                            int64_t c1, hipStream_t s) {
-  const int64_t n = (r1 - r0) * (c1 - c0);
-  if (n <= 0) return hipSuccess;
-  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
-  hipLaunchKernelGGL(k_zero_rect, dim3((unsigned)blocks), dim3(256), 0, s, p, ld, r0, r1, c0, c1);
   return hipGetLastError();
 }
 

@@ -795,7 +795,7 @@ RLK_API rlk_status_t rlk_logprob_backward(rlk_logprob_t h, const void* hidden, c
     a.lda = H;
     a.B = hin;
     a.ldb = H;
-    a.M = (int32_t)V;
+    a.M = (int32_t)m.J;  // over the segment-padded positions (writes the padding zeros)
     a.N = (int32_t)n;
     a.K = H;
     a.seg_len = m.L;
@@ -814,16 +814,6 @@ RLK_API rlk_status_t rlk_logprob_backward(rlk_logprob_t h, const void* hidden, c
     a.portable = (c.flags & RLK_FLAG_PORTABLE_EXP) ? 1 : 0;
     e = rlk::launch_gemm_dz(a, s);
     if (e != hipSuccess) return hip_fail(e, "dz launch");
-    for (int sg = 0; sg < S && m.Lp > m.L; ++sg) {
-      const int64_t p0 = sg * m.Lp + m.L, p1 = (sg + 1) * m.Lp;
-      if (want_h) e = rlk::launch_zero_rect(dz, m.J, 0, n, p0, p1, s);
-      if (e == hipSuccess && want_w) e = rlk::launch_zero_rect(dzt, np, p0, p1, 0, np, s);
-      if (e != hipSuccess) return hip_fail(e, "pad launch");
-    }
-    if (want_w && np > n) {
-      e = rlk::launch_zero_rect(dzt, np, 0, m.J, n, np, s);
-      if (e != hipSuccess) return hip_fail(e, "pad launch");
-    }
     if (want_h) {
       // B2: per segment chains, then the segment tree
       rlk::GemmArgs g{};

@@ -93,8 +93,9 @@ constexpr int kBwdKPad = 128;  // K of the backward GEMMs (vocab per segment, ro
 
 // NT GEMM tile kernel of the backward: acc[m, n] = sum_k A[m, k] B[n, k] (bf16, fp32 MFMA chain,
 // K ascending from +0 or from the stored output), then one of two epilogues.
-//  DZ:  A = W rows (m = vocab v), B = LM-head input rows (n = row t), K = H. Writes the bf16
-//       gradient of the tempered logits' loss (B1) to dz[t][col(v)] and dzt[col(v)][t].
+//  DZ:  m = segment-padded vocab position (M = S_c Lp; A row m is W row v(m)), B = LM-head input
+//       rows (n = row t), K = H. Writes the bf16 gradient of the tempered logits' loss (B1) to
+//       dz[t][m] and dzt[m][t], zeros at padding positions and at rows t >= N (up to lddzt).
 //  OUT: writes C[row(n) * ldc + m] in fp32 (dh: m = h, n = t; dW: m = h, n = padded vocab row).
 // col(v) / row(n) is the segment-padded vocab layout: v = s seg_len + c <-> s seg_pad + c.
 struct GemmArgs {
@@ -163,9 +164,6 @@ hipError_t launch_dgamma(const float* dy, const uint16_t* x, const float* r, flo
 hipError_t launch_gemm_dz(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_out(const GemmArgs& a, int batches, hipStream_t s);
 hipError_t launch_transpose(const TransposeArgs& a, hipStream_t s);
-// bf16 zeros over rows [r0, r1) x columns [c0, c1) of a matrix with row stride ld
-hipError_t launch_zero_rect(uint16_t* p, int64_t ld, int64_t r0, int64_t r1, int64_t c0,
-                            int64_t c1, hipStream_t s);
 // fp32 zeros over n elements (a fill kernel: usable under graph capture)
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
 // out[i] = balanced pairwise tree over s < nseg of part[s * stride + i] (nseg in 1, 2, 4, 8)
