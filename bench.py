@@ -48,7 +48,10 @@ PROFILE_STATS = os.path.join(ROOT, "profiles", "lmhead_qwen3_8b_head_kernel_stat
 NOMINAL_SCLK_MHZ = 2400.0  # the clock the published MFMA peak is quoted at
 PROF_ARGS = "--steps 3 --warmup 1 --no-cpu-baseline --no-layout-check --no-extras"
 STATS_ARGS = "--steps 30 --warmup 3 --no-cpu-baseline --no-layout-check --no-extras"
-KERNEL_SRC = os.path.join(ROOT, "invariant_lm_head_deterministic_amd", "csrc", "rlk_kernels.hip")
+# the sources the LM-head kernel is compiled from (its file, the shared K loop and primitives,
+# the argument structs): a change to any of them makes the committed PMC figures stale
+KERNEL_SRCS = [os.path.join(ROOT, "invariant_lm_head_deterministic_amd", "csrc", f)
+               for f in ("rlk_kernels.hip", "rlk_device.h", "rlk_internal.h")]
 
 
 def log(msg: str) -> None:
@@ -88,7 +91,10 @@ class HipEvents:
 
 
 def kernel_source_sha() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def committed_pmc() -> tuple[dict, str]:
