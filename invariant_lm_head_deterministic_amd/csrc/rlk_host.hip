@@ -694,7 +694,8 @@ RLK_API rlk_status_t rlk_logprob_backward(rlk_logprob_t h, const void* hidden, c
                                           size_t workspace_bytes, rlk_stream_t stream) {
   if (!h) return fail(RLK_ERR_INVALID_ARGUMENT, "handle is NULL");
   const rlk_logprob_config_t& c = h->cfg;
-  if (flags & ~RLK_BWD_ACCUMULATE) return fail(RLK_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", flags);
+  if (flags & ~(RLK_BWD_ACCUMULATE | RLK_BWD_REUSE_WT))
+    return fail(RLK_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", flags);
   rlk_status_t st = check_bwd_rows(c, num_rows, row_chunk);
   if (st != RLK_OK) return st;
   const bool rms = c.flags & RLK_FLAG_RMSNORM;
@@ -754,7 +755,7 @@ RLK_API rlk_status_t rlk_logprob_backward(rlk_logprob_t h, const void* hidden, c
   const uint16_t* gam = static_cast<const uint16_t*>(rms_gamma);
   const uint16_t* hid = static_cast<const uint16_t*>(hidden);
   const uint16_t* Wb = static_cast<const uint16_t*>(W_lm);
-  if (want_h) {
+  if (want_h && !(flags & RLK_BWD_REUSE_WT)) {
     rlk::TransposeArgs ta;
     ta.in = Wb;
     ta.ldi = H;
