@@ -388,7 +388,7 @@ def long_grpo(rlk, datagen, np, torch, Wd) -> dict:
 
 def backward(rlk, np, torch, hd, Wd, yd, w, steps: int = 5, warmup: int = 2) -> dict:
     """The backward at the headline shape: gradients of sum_t logp_t with respect to the hidden
-    rows and W (dz GEMM with its epilogue, W transpose, per-segment dh GEMM + tree, dW GEMM),
+    rows and W (dz GEMM with its epilogue, per-segment dh GEMM + tree, dW GEMM),
     timed on the stream with torch events; TFLOP/s counts the three GEMMs (3 x 2 T H V)."""
     dev = hd.device
     lp = rlk.Logprob(w.H, w.V, vocab_segments=w.segments, device=0)
@@ -406,17 +406,9 @@ def backward(rlk, np, torch, hd, Wd, yd, w, steps: int = 5, warmup: int = 2) -> 
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    # micro-batches of one optimizer step: W unchanged, its transpose kept in the workspace
-    e0.record()
-    for _ in range(steps):
-        lp.backward(hd, Wd, yd, fw["lse"], g, grad_W=gw, workspace=ws, reuse_wt=True)
-    e1.record()
-    torch.cuda.synchronize()
-    ms_reuse = e0.elapsed_time(e1) / steps
     fl = 3 * 2.0 * w.T * w.H * w.V
     del lp, ws, gw
-    return {"ms_per_step": ms, "ms_per_step_reusing_wt": ms_reuse,
-            "tokens_per_s": w.T / (ms * 1e-3),
+    return {"ms_per_step": ms, "tokens_per_s": w.T / (ms * 1e-3),
             "gemm_tflops": fl / (ms * 1e-3) / 1e12,
             "frac_of_bf16_peak": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
             "workspace_bytes": rlk.rlk_logprob_backward_workspace_size(

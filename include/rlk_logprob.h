@@ -205,16 +205,13 @@ const char* rlk_logprob_contract_id(rlk_logprob_t handle);
  *     grad_gamma = sum over rows of (dy x) r, as a chain over groups of 128 rows (from 0 or,
  *     with RLK_BWD_ACCUMULATE, from grad_gamma's contents). */
 #define RLK_BWD_ACCUMULATE 1u /* grad_W / grad_gamma continue their chains from their contents */
-/* The workspace already holds W_lm's transpose from an earlier call of this handle with the same
- * W_lm contents, the same workspace and a gradient w.r.t. the hidden rows (e.g. the micro-batches
- * of one optimizer step): it is not rebuilt. The caller vouches for this; a stale transpose gives
- * wrong gradients. */
-#define RLK_BWD_REUSE_WT 2u
 
 /* Workspace bytes for rlk_logprob_backward with both gradients requested (an upper bound for
- * fewer). row_chunk: 0 (all rows at once) or a positive multiple of 128. About
- * 2 V_pad (H + 2 rows_per_chunk) + 4 S_c rows_per_chunk H bytes (V_pad = V rounded up per
- * segment to 128), plus about 6 rows_per_chunk H bytes with RLK_FLAG_RMSNORM. */
+ * fewer). row_chunk: 0 (all rows at once) or a positive multiple of 128; rows are processed in
+ * chunks of at most that many rows, and of fewer when 2 V_pad bytes per row would pass 2 GiB
+ * (V_pad = V rounded up per segment to 128), which changes no result bit. About
+ * 2 V_pad rows_per_chunk + 4 S_c rows_per_chunk H bytes, plus about 10 rows_per_chunk H bytes
+ * with RLK_FLAG_RMSNORM. */
 rlk_status_t rlk_logprob_backward_workspace_size(const rlk_logprob_config_t* config,
                                                  int64_t num_rows, int64_t row_chunk,
                                                  size_t* bytes);
@@ -224,8 +221,7 @@ rlk_status_t rlk_logprob_backward_workspace_size(const rlk_logprob_config_t* con
  * rows under this handle. grad_logp fp32 [T]; grad_entropy fp32 [T] or NULL (needs
  * RLK_FLAG_ENTROPY). rms_gamma bf16 [H]: required with RLK_FLAG_RMSNORM, else NULL. Outputs
  * (each optional, at least one): grad_hidden fp32 [T, H], grad_W fp32 [V, H], grad_gamma fp32
- * [H] (RLK_FLAG_RMSNORM only). flags: RLK_BWD_ACCUMULATE (grad_W and grad_gamma continue),
- * RLK_BWD_REUSE_WT, or 0.
+ * [H] (RLK_FLAG_RMSNORM only). flags: RLK_BWD_ACCUMULATE (grad_W and grad_gamma continue) or 0.
  * All device pointers 16-byte aligned; the workspace (device, caller-owned) at least
  * rlk_logprob_backward_workspace_size() bytes. Enqueues on stream without synchronizing or
  * allocating. Errors are returned before anything is enqueued. */

@@ -15,7 +15,6 @@ import numpy as np
 from . import _lib
 from ._lib import (  # noqa: F401
     RLK_BWD_ACCUMULATE,
-    RLK_BWD_REUSE_WT,
     RLK_DEVICE_STATUS_BAD_TARGET,
     RLK_FLAG_ENTROPY,
     RLK_FLAG_PORTABLE_EXP,
@@ -234,15 +233,13 @@ class Logprob:
     def backward(self, hidden, W, targets, lse, grad_logp, *, entropy=None, grad_entropy=None,
                  gamma=None, want_hidden: bool = True, want_W: bool = True,
                  want_gamma: bool | None = None, grad_W=None, grad_gamma=None,
-                 accumulate: bool = False, reuse_wt: bool = False, row_chunk: int = 0,
-                 workspace=None, stream=None) -> dict:
+                 accumulate: bool = False, row_chunk: int = 0, workspace=None,
+                 stream=None) -> dict:
         """Gradients of sum_t grad_logp[t] logp[t] (+ grad_entropy[t] entropy[t]) with respect
         to the hidden rows ("grad_hidden", fp32 [T, H]; through the RMSNorm when the handle has
         one), W ("grad_W", fp32 [V, H]) and the RMSNorm's gamma ("grad_gamma", fp32 [H]).
         lse (and entropy) are the forward's outputs for these rows. grad_W / grad_gamma may be
-        given to write into; with accumulate=True their chains continue from their contents.
-        reuse_wt=True: `workspace` is the one of an earlier call with the same W contents, whose
-        transpose of W it still holds (see RLK_BWD_REUSE_WT)."""
+        given to write into; with accumulate=True their chains continue from their contents."""
         import torch
 
         bf = (torch.bfloat16, torch.int16, torch.uint16)
@@ -266,8 +263,6 @@ class Logprob:
         need = rlk_logprob_backward_workspace_size(self.config, T, row_chunk)
         if workspace is not None:
             self._check(workspace, (torch.uint8, torch.int8), "workspace")
-        if reuse_wt and (workspace is None or workspace.numel() < need):
-            raise ValueError("reuse_wt=True needs the earlier call's workspace")
         if workspace is None or workspace.numel() < need:
             workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
         out = {}
@@ -294,8 +289,7 @@ class Logprob:
                              _ptr(gamma), lse.data_ptr(), _ptr(entropy), grad_logp.data_ptr(),
                              _ptr(grad_entropy), _ptr(out.get("grad_hidden")),
                              _ptr(out.get("grad_W")), _ptr(out.get("grad_gamma")),
-                             (RLK_BWD_ACCUMULATE if accumulate else 0)
-                             | (RLK_BWD_REUSE_WT if reuse_wt else 0), row_chunk,
+                             RLK_BWD_ACCUMULATE if accumulate else 0, row_chunk,
                              workspace.data_ptr(), workspace.numel(), s.cuda_stream)
         out["_workspace"] = workspace
         return out

@@ -28,7 +28,6 @@ RLK_FLAG_RMSNORM = 1
 RLK_FLAG_ENTROPY = 2
 RLK_FLAG_PORTABLE_EXP = 4
 RLK_BWD_ACCUMULATE = 1
-RLK_BWD_REUSE_WT = 2
 RLK_DEVICE_STATUS_BAD_TARGET = 1
 
 

@@ -29,12 +29,12 @@
 //     from 0 or the stored dgamma, of P_q = sum over the group's rows ascending, from +0, of
 //     (dy_tk x_tk) r_t; row chunks of a multiple of 128 rows continue it.
 //
-// Layout of the backward's intermediates (all in the caller's workspace): dz [rows][S_c Lp] and
-// dzt [S_c Lp][rows padded] hold vocab index v = s L + c at the segment-padded position s Lp + c
-// (L = V / S_c, Lp = L rounded up to 128), with zeros at the padding positions and padding rows;
-// WT [H][S_c Lp] and hT [H][rows padded] are the transposed operands (zeros in their padding), so
-// every GEMM here is an NT GEMM with K contiguous in both operands, the shape of the forward's K
-// loop (nt_mainloop). The dz kernel runs over the padded positions, so it writes those zeros.
+// Layout: dz [rows][S_c Lp] (in the caller's workspace) holds vocab index v = s L + c at the
+// segment-padded position s Lp + c (L = V / S_c, Lp = L rounded up to 128), with zeros at the
+// padding positions; the dz kernel runs over the padded positions, so it writes those zeros.
+// All three GEMMs run on the forward's K loop (nt_mainloop). dh reads W as it is stored (K =
+// vocab index is its row index) and dW reads the hidden rows and dz as they are stored (K = row),
+// through the K loop's transposed staging (ds_read_b64_tr_b16): nothing is transposed in memory.
 
 #include <algorithm>
 #include <utility>
@@ -139,7 +139,7 @@ __device__ __forceinline__ uint16_t dz_one(float acc, int v, int y, float g, flo
 }
 
 // The backward's NT GEMM tile kernel (see GemmArgs). EPI 0 = DZ, 1 = OUT.
-template <int EPI, bool ENTG, bool TEMP, bool PORT, bool ACC>
+template <int EPI, bool ENTG, bool TEMP, bool PORT, bool ACC, bool ATR, bool BTR>
 __global__ void __launch_bounds__(64 * kGWaves) k_gemm(const GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds_a0[kGBM * kRowBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_a1[kGBM * kRowBytes];
@@ -154,7 +154,8 @@ __global__ void __launch_bounds__(64 * kGWaves) k_gemm(const GemmArgs a) {
   const int wv = wave % kGVW;
   const int wt = wave / kGVW;
   const int64_t yb = blockIdx.y;
-  const uint16_t* __restrict__ Bt = a.B + yb * a.b_batch + (int64_t)t.n0 * a.ldb;
+  const uint16_t* __restrict__ Bt =
+      BTR ? a.B + yb * a.b_batch + t.n0 : a.B + yb * a.b_batch + (int64_t)t.n0 * a.ldb;
 
   // Staging offsets as in the forward: rows past the tile are clamped to its last row. DZ runs
   // over the segment-padded vocab positions: tile row m reads W row v(m), a padding position
@@ -180,6 +181,9 @@ __global__ void __launch_bounds__(64 * kGWaves) k_gemm(const GemmArgs a) {
       const uint32_t v = vrow((uint32_t)(t.m0 + min(r, t.mrows - 1))) - vf;
       ago[q] = (uint32_t)(((int64_t)v * a.lda + c * 8) * 2);
     }
+  } else if constexpr (ATR) {
+    At = a.A + yb * a.a_batch + t.m0;
+    a_rows = 0;
   } else {
     At = a.A + yb * a.a_batch + (int64_t)t.m0 * a.lda;
     a_rows = t.mrows;
@@ -190,15 +194,42 @@ __global__ void __launch_bounds__(64 * kGWaves) k_gemm(const GemmArgs a) {
       ago[q] = (uint32_t)(((int64_t)min(r, t.mrows - 1) * a.lda + c * 8) * 2);
     }
   }
+  // A K-major (transposed) operand is staged 64 K rows x 256 indices per stage: DMA instruction q
+  // of this wave fills rows 2 (q NWAVES + wave) and the next, lane l slot l & 31 of its row,
+  // with the piece the swizzle puts there. Its descriptor spans the valid K rows only (and ends
+  // at the array's last element), so padding rows read as zeros.
+  auto tr_offsets = [&](uint32_t* go, int64_t ld) {
 #pragma unroll
-  for (int q = 0; q < kGHI; ++q) {
-    const int r = 8 * (q * kGWaves + wave) + (lane >> 3);
-    const int c = (lane & 7) ^ swz(r);
-    bgo[q] = (uint32_t)(((int64_t)min(r, t.nrows - 1) * a.ldb + c * 8) * 2);
+    for (int q = 0; q < 4; ++q) {
+      const int r = 2 * (q * kGWaves + wave) + (lane >> 5);
+      const int pc = (lane & 31) ^ tswz(r);
+      go[q] = (uint32_t)(((int64_t)r * ld + pc * 8) * 2);
+    }
+  };
+  auto tr_bytes = [&](int64_t krows, int64_t ld, int i0) {
+    return (int)(((krows - 1) * ld + min<int64_t>(256, ld - i0)) * 2);
+  };
+  if constexpr (ATR) {
+    static_assert(kGWI == 4, "64 K rows x 512 bytes per stage = 4 DMA instructions per wave");
+    tr_offsets(ago, a.lda);
   }
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(At, (int)(((a_rows - 1) * a.lda + a.K) * 2));
+  if constexpr (BTR) {
+    static_assert(kGHI == 4, "64 K rows x 512 bytes per stage = 4 DMA instructions per wave");
+    tr_offsets(bgo, a.ldb);
+  } else {
+#pragma unroll
+    for (int q = 0; q < kGHI; ++q) {
+      const int r = 8 * (q * kGWaves + wave) + (lane >> 3);
+      const int c = (lane & 7) ^ swz(r);
+      bgo[q] = (uint32_t)(((int64_t)min(r, t.nrows - 1) * a.ldb + c * 8) * 2);
+    }
+  }
+  const __amdgpu_buffer_rsrc_t ra =
+      ATR ? make_rsrc(At, tr_bytes(a.ka_rows, a.lda, t.m0))
+          : make_rsrc(At, (int)(((a_rows - 1) * a.lda + a.K) * 2));
   const __amdgpu_buffer_rsrc_t rb =
-      make_rsrc(Bt, (int)(((int64_t)(t.nrows - 1) * a.ldb + a.K) * 2));
+      BTR ? make_rsrc(Bt, tr_bytes(a.kb_rows, a.ldb, t.n0))
+          : make_rsrc(Bt, (int)(((int64_t)(t.nrows - 1) * a.ldb + a.K) * 2));
 
   float* __restrict__ C = EPI == 1 ? a.C + yb * a.c_batch : nullptr;
   f32x4 acc[kGVB16][kGNB16];
@@ -220,13 +251,15 @@ __global__ void __launch_bounds__(64 * kGWaves) k_gemm(const GemmArgs a) {
       });
     });
   }
-  nt_mainloop<kGWaves, kGVB16, kGNB16, kGWI, kGHI>(acc, lds_a0, lds_a1, lds_b0, lds_b1, ra, rb,
-                                                   ago, bgo, a.K / kKStage, wave, lane, wv, wt);
+  nt_mainloop<kGWaves, kGVB16, kGNB16, kGWI, kGHI, ATR, BTR>(
+      acc, lds_a0, lds_a1, lds_b0, lds_b1, ra, rb, ago, bgo, a.K / kKStage, wave, lane, wv, wt,
+      (uint32_t)(64 * a.lda * 2), (uint32_t)(64 * a.ldb * 2));
 
   // The epilogues index the accumulators with compile-time constants (static_for): a runtime
-  // index would move them to scratch. The lane id is read afresh (mbcnt) so that no index value
-  // computed before the K loop stays live across it.
-  const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  // index would move them to scratch. The lane id goes through an empty asm so that the compiler
+  // recomputes every address from it instead of keeping the prologue's alive across the K loop.
+  int ln = lane;
+  __asm__ volatile("" : "+v"(ln));
   if constexpr (EPI == 1) {
     // one output row pointer per B block (row(n) needs one division), then constant offsets
     static_for<kGNB16>([&](auto jc) {
@@ -255,18 +288,10 @@ __global__ void __launch_bounds__(64 * kGWaves) k_gemm(const GemmArgs a) {
       hj[j] = ENTG ? a.gH[n] : 0.0f;
       ej[j] = ENTG ? a.ent[n] : 0.0f;
     }
-    const int q = ln & 3;
-    const bool lo2 = q < 2;
-    // v_perm_b32 selectors of the quad transpose (bytes 0-3 from the second operand, 4-7 from
-    // the first): odd q takes the low halves, even q the high halves
-    const uint32_t ps2 = (q & 1) ? 0x05040100u : 0x07060302u;
-    const uint32_t pu0 = (q & 1) ? 0x03020504u : 0x05040100u;
-    const uint32_t pu1 = (q & 1) ? 0x03020706u : 0x07060100u;
-    // hoisted addressing: the lane's dz row for B block 0 (block j adds 16 rows) and the quad's
-    // first dzt column; positions, segments and vocab indices in 32-bit math (< 2^31)
+    // hoisted addressing: the lane's dz row for B block 0 (block j adds 16 rows); positions,
+    // segments and vocab indices in 32-bit math (< 2^31)
     const int64_t tl = t.n0 + 16 * wt * kGNB16 + (ln & 15);
-    const int64_t tq = t.n0 + 16 * wt * kGNB16 + (ln & 12);
-    uint16_t* const dzr = a.dz ? a.dz + tl * a.lddz : nullptr;
+    uint16_t* const dzr = a.dz + tl * a.lddz;
     const int64_t dz_j = 16 * a.lddz;
     const uint32_t L = (uint32_t)a.seg_len, Lp = (uint32_t)a.seg_pad;
     const uint32_t cb = (uint32_t)(t.m0 + 16 * wv * kGVB16 + 4 * (ln >> 4));
@@ -277,13 +302,11 @@ __global__ void __launch_bounds__(64 * kGWaves) k_gemm(const GemmArgs a) {
       const uint32_t sg = col0 / Lp;
       const uint32_t c0 = col0 - sg * Lp;  // position inside the segment
       const int v0 = (int)(sg * L + c0);   // vocab index of col0 when c0 < L
-      uint16_t* const dztr = a.dzt ? a.dzt + (int64_t)(col0 + q) * a.lddzt + tq : nullptr;
       const bool col_ok = (int)col0 < a.M;
       static_for<kGNB16>([&](auto jc) {
         constexpr int j = decltype(jc)::value;
         const int nn = 16 * (wt * kGNB16 + j) + (ln & 15);
-        // every lane computes (rows past the tile have y = -1, padding positions give 0), so
-        // the quad exchange below runs with all lanes active
+        if (nn >= t.nrows || !col_ok) return;
         uint16_t b[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -293,54 +316,9 @@ __global__ void __launch_bounds__(64 * kGWaves) k_gemm(const GemmArgs a) {
         }
         const uint32_t w0 = (uint32_t)b[0] | ((uint32_t)b[1] << 16);
         const uint32_t w1 = (uint32_t)b[2] | ((uint32_t)b[3] << 16);
-        if (dzr && nn < t.nrows && col_ok) *(uint2*)(dzr + j * dz_j + col0) = make_uint2(w0, w1);
-        if (dztr) {
-          // A quad (lanes 4k .. 4k+3) holds the 4 x 4 block dz[col0 + r][t0 + lane & 3]; two
-          // exchanges transpose it, so lane q ends with dz[col0 + q][t0 .. t0+3] for one 8-byte
-          // store. Step 1 swaps row pairs across q ^ 2, step 2 single elements across q ^ 1.
-          const uint32_t k1 = lo2 ? w0 : w1;
-          const uint32_t s1 = lo2 ? w1 : w0;
-          const uint32_t r1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)s1, 0x4E, 0xf, 0xf, false);
-          const uint32_t A = lo2 ? k1 : r1;  // rows R, R+1 at column q & 1
-          const uint32_t B = lo2 ? r1 : k1;  // rows R, R+1 at column (q & 1) + 2
-          // odd q sends (A.lo, B.lo), even q (A.hi, B.hi); then each keeps its own half and
-          // places the received one (byte selects of v_perm_b32, per-lane selectors)
-          const uint32_t s2 = __builtin_amdgcn_perm(B, A, ps2);
-          const uint32_t r2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)s2, 0xB1, 0xf, 0xf, false);
-          const uint32_t u0 = __builtin_amdgcn_perm(r2, A, pu0);
-          const uint32_t u1 = __builtin_amdgcn_perm(r2, B, pu1);
-          if (col_ok && tq + 16 * j < a.lddzt) *(uint2*)(dztr + 16 * j) = make_uint2(u0, u1);
-        }
+        *(uint2*)(dzr + j * dz_j + col0) = make_uint2(w0, w1);
       });
     });
-  }
-}
-
-// 64 x 64 transpose tile through LDS (see TransposeArgs). The tile is stored as [c][j] so that
-// the output rows leave LDS as 16-byte vectors and 8 lanes write 128 contiguous bytes.
-__global__ void __launch_bounds__(256) k_transpose(const TransposeArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];
-  const int64_t j0 = (int64_t)blockIdx.x * 64;
-  const int64_t c0 = (int64_t)blockIdx.y * 64;
-  for (int q = threadIdx.x; q < 64 * 8; q += 256) {
-    const int jj = q >> 3, pc = q & 7;
-    const int64_t j = j0 + jj;
-    const int64_t s = j / a.Lp, cc = j - s * a.Lp;
-    const int64_t r = s * a.L + cc;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (j < a.J && cc < a.L && r < a.R) v = *(const u32x4*)(a.in + r * a.ldi + c0 + pc * 8);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      tile[pc * 8 + 2 * e][jj] = (uint16_t)(v[e] & 0xffffu);
-      tile[pc * 8 + 2 * e + 1][jj] = (uint16_t)(v[e] >> 16);
-    }
-  }
-  __syncthreads();
-  for (int q = threadIdx.x; q < 64 * 8; q += 256) {
-    const int cr = q >> 3, pj = q & 7;
-    const int64_t j = j0 + pj * 8;
-    if (j >= a.J) continue;
-    *(u32x4*)(a.out + (c0 + cr) * a.ldo + j) = *(const u32x4*)(&tile[cr][pj * 8]);
   }
 }
 
@@ -494,28 +472,25 @@ hipError_t launch_gemm_dz(const GemmArgs& a, hipStream_t s) {
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   with_bwd_modes(a.gH != nullptr, a.inv_tau != 1.0f, a.portable != 0,
                  [&](auto e, auto t, auto p) {
-                   hipLaunchKernelGGL((k_gemm<0, e.value, t.value, p.value, false>),
+                   hipLaunchKernelGGL((k_gemm<0, e.value, t.value, p.value, false, false, false>),
                                       dim3((unsigned)blocks), dim3(64 * kGWaves), 0, s, a);
                  });
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_out(const GemmArgs& a, int batches, hipStream_t s) {
+hipError_t launch_gemm_out(const GemmArgs& a, int batches, bool b_trans, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0 || batches <= 0) return hipSuccess;
   const int64_t blocks = gemm_blocks(a.M, a.N);
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  const dim3 grid((unsigned)blocks, (unsigned)batches);
-  if (a.accumulate)
-    hipLaunchKernelGGL((k_gemm<1, false, false, false, true>), grid, dim3(64 * kGWaves), 0, s, a);
-  else
-    hipLaunchKernelGGL((k_gemm<1, false, false, false, false>), grid, dim3(64 * kGWaves), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_transpose(const TransposeArgs& a, hipStream_t s) {
-  if (a.J <= 0 || a.C <= 0) return hipSuccess;
-  const dim3 grid((unsigned)((a.J + 63) / 64), (unsigned)((a.C + 63) / 64));
-  hipLaunchKernelGGL(k_transpose, grid, dim3(256), 0, s, a);
+  const dim3 grid((unsigned)blocks, (unsigned)batches), block(64 * kGWaves);
+  // dh: A (W) K-major, B (dz) K-contiguous; dW: both K-major (hidden rows, dz)
+  if (b_trans) {
+    if (a.accumulate) hipLaunchKernelGGL((k_gemm<1, false, false, false, true, true, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_gemm<1, false, false, false, false, true, true>), grid, block, 0, s, a);
+  } else {
+    if (a.accumulate) hipLaunchKernelGGL((k_gemm<1, false, false, false, true, true, false>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_gemm<1, false, false, false, false, true, false>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 

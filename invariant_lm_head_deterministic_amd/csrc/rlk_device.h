@@ -184,18 +184,68 @@ __device__ __forceinline__ float tree_sum(const float* v) {
 // has landed everywhere, and every read of stage k's buffer is done); sub-step 1 then issues the
 // DMA of stage k+2 into stage k's buffer and reads the first fragments of stage k+1. The last two
 // stages issue no DMA and their final fragment reads are unused (in bounds).
-template <int NWAVES, int VB16, int NB16, int WI, int HI>
+// K-major ("transposed") staging of an operand, for operands stored with K as the row index
+// (the backward's W, hidden rows and dz): a stage holds 64 K rows of the block's 256 M (or N)
+// indices, 512 bytes per row, and piece p (8 indices) of row r sits at slot p ^ tswz(r). A
+// fragment is read with two ds_read_b64_tr_b16 (gfx950's transposing LDS load: within each 16
+// lanes, source lane 4k + q supplies 4 consecutive values and lane i receives value i % 4 of
+// source 4k + i / 4, k = 0..3 - pinned by a probe): source lane j of lane group g reads row
+// 8g + j / 4 (and 4 rows further for the second read) at the 4 indices from 4 (j % 4), so lane
+// i of group g receives K rows 8g .. 8g+7 of index i: the MFMA operand layout. The 16 rows one
+// read touches (4 per group, groups 8 rows apart) take 8 swizzle values twice each, the 2-way
+// minimum of a 512-byte read over 64 banks.
+constexpr int kTRowBytes = 512;
+__device__ __forceinline__ int tswz(int r) { return 2 * ((r & 3) | ((r >> 1) & 4)); }
+
+__device__ __forceinline__ bf16x8 tr_read(const uint8_t* tile, int off) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef short v8s __attribute__((ext_vector_type(8)));
+  typedef __attribute__((address_space(3))) v4s* lv4s;
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lv4s)(tile + off));
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lv4s)(tile + off + 4 * kTRowBytes));
+  const v8s c = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, c);
+}
+
+// Per-lane byte offset (sub-step 0, block 0) and block XOR of transposed fragment reads: block
+// b of sub-step s is read at base + 16384 s + ((32 b) ^ x).
+__device__ __forceinline__ void tr_lane(int lane, int& base, int& x) {
+  const int j = lane & 15, g = lane >> 4;
+  const int row = 8 * g + (j >> 2);
+  base = row * kTRowBytes + 16 * ((j & 3) >> 1) + 8 * (j & 1);
+  x = 16 * tswz(row);
+}
+
+template <int NWAVES, int VB16, int NB16, int WI, int HI, bool ATR = false, bool BTR = false>
 __device__ __forceinline__ void nt_mainloop(f32x4 (&acc)[VB16][NB16], uint8_t* lds_w0,
                                             uint8_t* lds_w1, uint8_t* lds_h0, uint8_t* lds_h1,
                                             __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rh,
                                             const uint32_t (&wgo)[WI], const uint32_t (&hgo)[HI],
-                                            int nk, int wave, int lane, int wv, int wt) {
+                                            int nk, int wave, int lane, int wv, int wt,
+                                            uint32_t sa = 0, uint32_t sb = 0) {
+  // sa / sb: bytes from one K stage to the next of a transposed operand (64 rows)
   auto issue = [&](int kc, uint8_t* lw, uint8_t* lh) {
     const uint32_t so = (uint32_t)kc * kRowBytes;
+    const uint32_t soa = ATR ? (uint32_t)kc * sa : so;
+    const uint32_t sob = BTR ? (uint32_t)kc * sb : so;
 #pragma unroll
-    for (int q = 0; q < WI; ++q) dma16(rw, lw + 8 * (q * NWAVES + wave) * kRowBytes, wgo[q], so);
+    for (int q = 0; q < WI; ++q) dma16(rw, lw + 8 * (q * NWAVES + wave) * kRowBytes, wgo[q], soa);
 #pragma unroll
-    for (int q = 0; q < HI; ++q) dma16(rh, lh + 8 * (q * NWAVES + wave) * kRowBytes, hgo[q], so);
+    for (int q = 0; q < HI; ++q) dma16(rh, lh + 8 * (q * NWAVES + wave) * kRowBytes, hgo[q], sob);
+  };
+  int tbase = 0, tx = 0;
+  if constexpr (ATR || BTR) tr_lane(lane, tbase, tx);
+  auto fragA = [&](const uint8_t* lw, int ns, int i) -> bf16x8 {
+    if constexpr (ATR) return tr_read(lw, 16384 * ns + tbase + ((32 * (wv * VB16 + i)) ^ tx));
+    else return *(const bf16x8*)(lw + 16 * wv * VB16 * kRowBytes + i * 16 * kRowBytes +
+                                 (lane & 15) * kRowBytes +
+                                 (((4 * ns + (lane >> 4)) ^ swz(lane & 15)) << 4));
+  };
+  auto fragB = [&](const uint8_t* lh, int ns, int j) -> bf16x8 {
+    if constexpr (BTR) return tr_read(lh, 16384 * ns + tbase + ((32 * (wt * NB16 + j)) ^ tx));
+    else return *(const bf16x8*)(lh + 16 * wt * NB16 * kRowBytes + j * 16 * kRowBytes +
+                                 (lane & 15) * kRowBytes +
+                                 (((4 * ns + (lane >> 4)) ^ swz(lane & 15)) << 4));
   };
 
   // Fragment reads: sub-step s (K 32s .. 32s+31 of a stage) reads piece 4s + (lane >> 4) of row
@@ -219,13 +269,17 @@ __device__ __forceinline__ void nt_mainloop(f32x4 (&acc)[VB16][NB16], uint8_t* l
     const uint8_t* pa = lw + a0 + loff[ns];
     const uint8_t* pb = lh + b0 + loff[ns];
 #pragma unroll
-    for (int j = 0; j < NB16; ++j) fb[1 - cb][j] = *(const bf16x8*)(pb + j * 16 * kRowBytes);
+    for (int j = 0; j < NB16; ++j) {
+      if constexpr (BTR) fb[1 - cb][j] = fragB(lh, ns, j);
+      else fb[1 - cb][j] = *(const bf16x8*)(pb + j * 16 * kRowBytes);
+    }
 #pragma unroll
     for (int i = 0; i < VB16; ++i) {
 #pragma unroll
       for (int j = 0; j < NB16; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[cb][j], acc[i][j], 0, 0, 0);
-      fa[i] = *(const bf16x8*)(pa + i * 16 * kRowBytes);
+      if constexpr (ATR) fa[i] = fragA(lw, ns, i);
+      else fa[i] = *(const bf16x8*)(pa + i * 16 * kRowBytes);
     }
     // order: the B reads interleaved with the first row block's MFMAs, then one A read after
     // each row block; DMA instructions every EV MFMAs
@@ -235,8 +289,8 @@ __device__ __forceinline__ void nt_mainloop(f32x4 (&acc)[VB16][NB16], uint8_t* l
 #pragma unroll
     for (int n = 0; n < NM; ++n) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (n < NB16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (n % NB16 == NB16 - 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (n < NB16) __builtin_amdgcn_sched_group_barrier(0x100, BTR ? 2 : 1, 0);
+      if (n % NB16 == NB16 - 1) __builtin_amdgcn_sched_group_barrier(0x100, ATR ? 2 : 1, 0);
       if (ND > 0 && n % EV == EV - 1 && n / EV < INLOOP)
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
@@ -268,9 +322,15 @@ __device__ __forceinline__ void nt_mainloop(f32x4 (&acc)[VB16][NB16], uint8_t* l
     const uint8_t* pa = lds_w0 + a0 + loff[0];
     const uint8_t* pb = lds_h0 + b0 + loff[0];
 #pragma unroll
-    for (int j = 0; j < NB16; ++j) fb[0][j] = *(const bf16x8*)(pb + j * 16 * kRowBytes);
+    for (int j = 0; j < NB16; ++j) {
+      if constexpr (BTR) fb[0][j] = fragB(lds_h0, 0, j);
+      else fb[0][j] = *(const bf16x8*)(pb + j * 16 * kRowBytes);
+    }
 #pragma unroll
-    for (int i = 0; i < VB16; ++i) fa[i] = *(const bf16x8*)(pa + i * 16 * kRowBytes);
+    for (int i = 0; i < VB16; ++i) {
+      if constexpr (ATR) fa[i] = fragA(lds_w0, 0, i);
+      else fa[i] = *(const bf16x8*)(pa + i * 16 * kRowBytes);
+    }
   }
   // nothing scalar left in flight when the loop starts: a pending scalar load there makes every
   // iteration wait for all LDS reads (lgkmcnt(0)) instead of only the oldest fragments. The

@@ -619,22 +619,30 @@ namespace {
 
 struct BwdMap {
   int64_t L, Lp, J;    // segment length, padded length, padded vocab width S_c Lp
-  int64_t chunk, Tp;   // rows per chunk, chunk rows padded to kBwdKPad
-  size_t wt, dz, dzt, ht, dpart, y, dy, r, gp, total;
+  int64_t chunk;       // rows per chunk
+  size_t dz, dpart, y, dy, r, gp, total;
 };
 
+// Rows per chunk: the caller's row_chunk (or all rows), capped so that the dz rows of a chunk
+// span less than 2 GiB (the 32-bit range of the GEMMs' buffer descriptors). Any multiple of 128
+// gives the same bits (B3, B4), so the cap changes no result.
+int64_t bwd_chunk(int64_t rows, int64_t row_chunk, int64_t J) {
+  const int64_t r = std::max<int64_t>(rows, 1);
+  int64_t c = row_chunk > 0 ? std::min<int64_t>(row_chunk, r) : r;
+  const int64_t cap = std::max<int64_t>((0x7fffffffLL / (2 * J)) / rlk::kBwdKPad * rlk::kBwdKPad,
+                                        rlk::kBwdKPad);
+  return std::min(c, cap);
+}
+
 // want_h: a gradient w.r.t. the LM-head input is needed (grad_hidden, or grad_gamma through the
-// RMSNorm); want_w: grad_W.
-BwdMap bwd_map(const rlk_logprob_config_t& c, int64_t rows, int64_t row_chunk, bool want_h,
-               bool want_w) {
+// RMSNorm).
+BwdMap bwd_map(const rlk_logprob_config_t& c, int64_t rows, int64_t row_chunk, bool want_h) {
   BwdMap m;
   const int S = c.vocab_segments;
   m.L = c.vocab_size / S;
   m.Lp = (int64_t)round_up((size_t)m.L, rlk::kBwdKPad);
   m.J = S * m.Lp;
-  const int64_t r = std::max<int64_t>(rows, 1);
-  m.chunk = row_chunk > 0 ? std::min<int64_t>(row_chunk, r) : r;
-  m.Tp = (int64_t)round_up((size_t)m.chunk, rlk::kBwdKPad);
+  m.chunk = bwd_chunk(rows, row_chunk, m.J);
   const size_t H = (size_t)c.hidden_size;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -642,10 +650,7 @@ BwdMap bwd_map(const rlk_logprob_config_t& c, int64_t rows, int64_t row_chunk, b
     off = round_up(off + bytes, 256);
     return at;
   };
-  m.wt = want_h ? take(H * (size_t)m.J * 2) : 0;
-  m.dz = want_h ? take((size_t)m.chunk * (size_t)m.J * 2) : 0;
-  m.dzt = want_w ? take((size_t)m.J * (size_t)m.Tp * 2) : 0;
-  m.ht = want_w ? take(H * (size_t)m.Tp * 2) : 0;
+  m.dz = take((size_t)m.chunk * (size_t)m.J * 2);
   m.dpart = (want_h && S > 1) ? take((size_t)S * (size_t)m.chunk * H * 4) : 0;
   const bool rms = c.flags & RLK_FLAG_RMSNORM;
   m.y = rms ? take((size_t)m.chunk * H * 2) : 0;
@@ -663,10 +668,12 @@ rlk_status_t check_bwd_rows(const rlk_logprob_config_t& c, int64_t num_rows, int
   if (row_chunk < 0 || (row_chunk > 0 && row_chunk % rlk::kBwdKPad != 0))
     return fail(RLK_ERR_UNSUPPORTED_SHAPE, "row_chunk %lld is not 0 or a positive multiple of %d",
                 (long long)row_chunk, rlk::kBwdKPad);
-  const BwdMap m = bwd_map(c, num_rows, row_chunk, true, true);
-  // 32-bit buffer ranges of the GEMM tiles: 256 rows of the widest operand
-  if ((int64_t)256 * std::max<int64_t>(m.J, m.Tp) * 2 >= 0x7fffffffLL)
-    return fail(RLK_ERR_UNSUPPORTED_SHAPE, "rows per chunk or padded vocab too large");
+  const BwdMap m = bwd_map(c, num_rows, row_chunk, true);
+  // 32-bit buffer ranges: one vocab segment of W (the dh GEMM's K-major operand), 256 rows of
+  // dz, and 128 rows of dz
+  if (m.Lp * (int64_t)c.hidden_size * 2 >= 0x7fffffffLL || 256 * m.J * 2 >= 0x7fffffffLL ||
+      (int64_t)rlk::kBwdKPad * m.J * 2 >= 0x7fffffffLL)
+    return fail(RLK_ERR_UNSUPPORTED_SHAPE, "vocab segment x hidden size too large for the backward");
   return RLK_OK;
 }
 
@@ -680,7 +687,7 @@ RLK_API rlk_status_t rlk_logprob_backward_workspace_size(const rlk_logprob_confi
   if (st != RLK_OK) return st;
   st = check_bwd_rows(*config, num_rows, row_chunk);
   if (st != RLK_OK) return st;
-  *bytes = bwd_map(*config, num_rows, row_chunk, true, true).total;
+  *bytes = bwd_map(*config, num_rows, row_chunk, true).total;
   return ok();
 }
 
@@ -694,7 +701,7 @@ RLK_API rlk_status_t rlk_logprob_backward(rlk_logprob_t h, const void* hidden, c
                                           size_t workspace_bytes, rlk_stream_t stream) {
   if (!h) return fail(RLK_ERR_INVALID_ARGUMENT, "handle is NULL");
   const rlk_logprob_config_t& c = h->cfg;
-  if (flags & ~(RLK_BWD_ACCUMULATE | RLK_BWD_REUSE_WT))
+  if (flags & ~RLK_BWD_ACCUMULATE)
     return fail(RLK_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", flags);
   rlk_status_t st = check_bwd_rows(c, num_rows, row_chunk);
   if (st != RLK_OK) return st;
@@ -719,7 +726,7 @@ RLK_API rlk_status_t rlk_logprob_backward(rlk_logprob_t h, const void* hidden, c
       !aligned16(grad_hidden) || !aligned16(grad_W) || !aligned16(workspace) ||
       !aligned16(rms_gamma) || !aligned16(grad_gamma))
     return fail(RLK_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
-  const BwdMap m = bwd_map(c, num_rows, row_chunk, want_h, want_w);
+  const BwdMap m = bwd_map(c, num_rows, row_chunk, want_h);
   if (!workspace || workspace_bytes < m.total)
     return fail(RLK_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", m.total,
                 workspace_bytes);
@@ -743,10 +750,7 @@ RLK_API rlk_status_t rlk_logprob_backward(rlk_logprob_t h, const void* hidden, c
     }
     return ok();
   }
-  uint16_t* WT = reinterpret_cast<uint16_t*>(ws + m.wt);
   uint16_t* dz = reinterpret_cast<uint16_t*>(ws + m.dz);
-  uint16_t* dzt = reinterpret_cast<uint16_t*>(ws + m.dzt);
-  uint16_t* hT = reinterpret_cast<uint16_t*>(ws + m.ht);
   float* dpart = reinterpret_cast<float*>(ws + m.dpart);
   uint16_t* ynorm = reinterpret_cast<uint16_t*>(ws + m.y);
   float* dy = reinterpret_cast<float*>(ws + m.dy);
@@ -755,20 +759,6 @@ RLK_API rlk_status_t rlk_logprob_backward(rlk_logprob_t h, const void* hidden, c
   const uint16_t* gam = static_cast<const uint16_t*>(rms_gamma);
   const uint16_t* hid = static_cast<const uint16_t*>(hidden);
   const uint16_t* Wb = static_cast<const uint16_t*>(W_lm);
-  if (want_h && !(flags & RLK_BWD_REUSE_WT)) {
-    rlk::TransposeArgs ta;
-    ta.in = Wb;
-    ta.ldi = H;
-    ta.R = V;
-    ta.C = H;
-    ta.out = WT;
-    ta.ldo = m.J;
-    ta.J = m.J;
-    ta.L = m.L;
-    ta.Lp = m.Lp;
-    e = rlk::launch_transpose(ta, s);
-    if (e != hipSuccess) return hip_fail(e, "transpose launch");
-  }
   int64_t chunk_no = 0;
   for (int64_t r0 = 0; r0 < num_rows; r0 += m.chunk, ++chunk_no) {
     const int64_t r1 = std::min<int64_t>(num_rows, r0 + m.chunk);
@@ -790,13 +780,13 @@ RLK_API rlk_status_t rlk_logprob_backward(rlk_logprob_t h, const void* hidden, c
       if (e != hipSuccess) return hip_fail(e, "rmsnorm launch");
       hin = ynorm;
     }
-    // B1: dz and its transpose
+    // B1: dz over the segment-padded positions (it writes the padding zeros)
     rlk::GemmArgs a{};
     a.A = Wb;
     a.lda = H;
     a.B = hin;
     a.ldb = H;
-    a.M = (int32_t)m.J;  // over the segment-padded positions (writes the padding zeros)
+    a.M = (int32_t)m.J;
     a.N = (int32_t)n;
     a.K = H;
     a.seg_len = m.L;
@@ -806,21 +796,21 @@ RLK_API rlk_status_t rlk_logprob_backward(rlk_logprob_t h, const void* hidden, c
     a.ent = grad_entropy ? entropy + r0 : nullptr;
     a.g = grad_logp + r0;
     a.gH = grad_entropy ? grad_entropy + r0 : nullptr;
-    a.dz = want_h ? dz : nullptr;
+    a.dz = dz;
     a.lddz = m.J;
-    a.dzt = want_w ? dzt : nullptr;
-    a.lddzt = np;
     a.V = V;
     a.inv_tau = c.inv_temperature;
     a.portable = (c.flags & RLK_FLAG_PORTABLE_EXP) ? 1 : 0;
     e = rlk::launch_gemm_dz(a, s);
     if (e != hipSuccess) return hip_fail(e, "dz launch");
     if (want_h) {
-      // B2: per segment chains, then the segment tree
+      // B2: per segment one chain over its positions (W read K-major, rows past the segment read
+      // as zeros), then the segment tree
       rlk::GemmArgs g{};
-      g.A = WT;
-      g.lda = m.J;
-      g.a_batch = m.Lp;
+      g.A = Wb;
+      g.lda = H;
+      g.a_batch = m.L * H;
+      g.ka_rows = m.L;
       g.B = dz;
       g.ldb = m.J;
       g.b_batch = m.Lp;
@@ -831,7 +821,7 @@ RLK_API rlk_status_t rlk_logprob_backward(rlk_logprob_t h, const void* hidden, c
       g.C = S > 1 ? dpart : dh;
       g.ldc = H;
       g.c_batch = n * H;
-      e = rlk::launch_gemm_out(g, S, s);
+      e = rlk::launch_gemm_out(g, S, false, s);
       if (e != hipSuccess) return hip_fail(e, "dh launch");
       if (S > 1) {
         e = rlk::launch_seg_tree(dpart, n * H, S, dh, n * H, s);
@@ -860,24 +850,15 @@ RLK_API rlk_status_t rlk_logprob_backward(rlk_logprob_t h, const void* hidden, c
       }
     }
     if (want_w) {
-      // B3: the chain over rows continues from the previous chunk
-      rlk::TransposeArgs ta;
-      ta.in = hin;
-      ta.ldi = H;
-      ta.R = n;
-      ta.C = H;
-      ta.out = hT;
-      ta.ldo = np;
-      ta.J = np;
-      ta.L = n;
-      ta.Lp = np;
-      e = rlk::launch_transpose(ta, s);
-      if (e != hipSuccess) return hip_fail(e, "transpose launch");
+      // B3: the hidden rows and dz read K-major (K = row, rows past the chunk read as zeros);
+      // the chain over rows continues from the previous chunk
       rlk::GemmArgs g{};
-      g.A = hT;
-      g.lda = np;
-      g.B = dzt;
-      g.ldb = np;
+      g.A = hin;
+      g.lda = H;
+      g.ka_rows = n;
+      g.B = dz;
+      g.ldb = m.J;
+      g.kb_rows = n;
       g.M = H;
       g.N = (int32_t)m.J;
       g.K = (int32_t)np;
@@ -887,7 +868,7 @@ RLK_API rlk_status_t rlk_logprob_backward(rlk_logprob_t h, const void* hidden, c
       g.ldc = H;
       g.accumulate = (accumulate || chunk_no > 0) ? 1 : 0;
       g.map_rows = 1;
-      e = rlk::launch_gemm_out(g, 1, s);
+      e = rlk::launch_gemm_out(g, 1, true, s);
       if (e != hipSuccess) return hip_fail(e, "dW launch");
     }
   }

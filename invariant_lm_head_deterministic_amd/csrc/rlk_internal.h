@@ -95,8 +95,11 @@ constexpr int kBwdKPad = 128;  // K of the backward GEMMs (vocab per segment, ro
 // K ascending from +0 or from the stored output), then one of two epilogues.
 //  DZ:  m = segment-padded vocab position (M = S_c Lp; A row m is W row v(m)), B = LM-head input
 //       rows (n = row t), K = H. Writes the bf16 gradient of the tempered logits' loss (B1) to
-//       dz[t][m] and dzt[m][t], zeros at padding positions and at rows t >= N (up to lddzt).
+//       dz[t][m], zeros at padding positions.
 //  OUT: writes C[row(n) * ldc + m] in fp32 (dh: m = h, n = t; dW: m = h, n = padded vocab row).
+//       A is K-major (row k of A holds the M indices: W for dh, the hidden rows for dW; ka_rows
+//       valid K rows, lda its row stride); B is K-contiguous (dz rows, dh) or K-major (dz, dW;
+//       kb_rows valid K rows). K-major rows past the valid ones read as zeros.
 // col(v) / row(n) is the segment-padded vocab layout: v = s seg_len + c <-> s seg_pad + c.
 struct GemmArgs {
   const uint16_t* A;
@@ -113,32 +116,20 @@ struct GemmArgs {
   int64_t a_batch, b_batch; // A / B offsets per blockIdx.y
   int32_t accumulate;       // start the chain from C's stored values
   int32_t map_rows;         // OUT rows n are segment-padded vocab rows (skip padding rows)
+  int64_t ka_rows, kb_rows; // valid K rows of a K-major A / B
   // DZ
   const int32_t* targets;   // [rows]
   const float* lse;         // forward lse [rows]
   const float* ent;         // forward entropy [rows] (with grad_ent)
   const float* g;           // dL/dlogp [rows]
   const float* gH;          // dL/dentropy [rows] or null
-  uint16_t* dz;             // bf16 [rows][S_c Lp] or null
+  uint16_t* dz;             // bf16 [rows][S_c Lp]
   int64_t lddz;
-  uint16_t* dzt;            // bf16 [S_c Lp][lddzt] or null
-  int64_t lddzt;
   int64_t V;
   float inv_tau;
   int32_t portable;
 };
 
-// out[c][j] (bf16, row stride ldo) = in[r(j)][c] for the segment-padded column j of row r(j)
-// (j = s Lp + cc, r = s L + cc, cc < L, r < R), else +0; c < C, j < J.
-struct TransposeArgs {
-  const uint16_t* in;
-  int64_t ldi;
-  int64_t R, C;
-  uint16_t* out;
-  int64_t ldo;
-  int64_t J;
-  int64_t L, Lp;
-};
 
 // B4: the final RMSNorm's backward, one wave per row. dx (optional) and r (optional) per row.
 struct RmsBwdArgs {
@@ -162,8 +153,7 @@ hipError_t launch_dgamma(const float* dy, const uint16_t* x, const float* r, flo
                          int H, float* dgamma, bool accumulate, hipStream_t s);
 
 hipError_t launch_gemm_dz(const GemmArgs& a, hipStream_t s);
-hipError_t launch_gemm_out(const GemmArgs& a, int batches, hipStream_t s);
-hipError_t launch_transpose(const TransposeArgs& a, hipStream_t s);
+hipError_t launch_gemm_out(const GemmArgs& a, int batches, bool b_trans, hipStream_t s);
 // fp32 zeros over n elements (a fill kernel: usable under graph capture)
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
 // out[i] = balanced pairwise tree over s < nseg of part[s * stride + i] (nseg in 1, 2, 4, 8)

@@ -165,11 +165,13 @@ def test_backward_workspace_size(lib):
     n = _lib.rlk_logprob_backward_workspace_size(cfg, 4096, 0)
     Lp = 38016  # 37984 rounded up to 128
     J = 4 * Lp
-    want = 4096 * J * 2 + 4096 * J * 2 + J * 4096 * 2 + 4096 * 4096 * 2 + 4 * 4096 * 4096 * 4
-    assert want <= n < want + 6 * 256
-    # chunked: the per-chunk buffers shrink, the transposed W does not
+    want = 4096 * J * 2 + 4 * 4096 * 4096 * 4  # dz rows, per-segment dh partials
+    assert want <= n < want + 2 * 256
     m = _lib.rlk_logprob_backward_workspace_size(cfg, 4096, 1024)
-    assert m < n and m >= 4096 * J * 2
+    assert 1024 * J * 2 + 4 * 1024 * 4096 * 4 <= m < n
+    # long batches are chunked so that a chunk's dz stays under 2 GiB: 7040 rows here
+    big = _lib.rlk_logprob_backward_workspace_size(cfg, 55296, 0)
+    assert 7040 * J * 2 <= big < 7040 * J * 2 + 4 * 7040 * 4096 * 4 + 2 * 256
     for bad in (100, -128):
         with pytest.raises(_lib.RlkError) as e:
             _lib.rlk_logprob_backward_workspace_size(cfg, 4096, bad)
