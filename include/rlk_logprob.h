@@ -233,6 +233,51 @@ rlk_status_t rlk_logprob_backward(rlk_logprob_t handle, const void* hidden, cons
                                   uint32_t flags, int64_t row_chunk, void* workspace,
                                   size_t workspace_bytes, rlk_stream_t stream);
 
+/* ---- Backward over vocab shards ------------------------------------------------------------
+ * The backward split the way a vocab-parallel (TP) run splits it: each shard computes, for its
+ * whole segments, the per-segment dh partials of B2 (before the tree) and its rows of grad_W;
+ * the merge then applies B2's segment tree (and, with RLK_FLAG_RMSNORM, B4) to the gathered
+ * partials. The result equals rlk_logprob_backward's bit for bit, for any split into shards
+ * (the "cross-TP vocab merge" and "fixed rank order" items of the ROCm fixes list on the
+ * RL-Kernel v0.1.0 summary page, applied to the gradient). */
+
+/* Host-only: workspace bytes of rlk_logprob_backward_partials for the vocab range
+ * [vocab_begin, vocab_end) (whole segments) and row_chunk (as rlk_logprob_backward). */
+rlk_status_t rlk_logprob_backward_partials_workspace_size(const rlk_logprob_config_t* config,
+                                                          int64_t num_rows, int64_t vocab_begin,
+                                                          int64_t vocab_end, int64_t row_chunk,
+                                                          size_t* bytes);
+
+/* One vocab shard's backward. W_shard: bf16 rows [vocab_begin, vocab_end) of W_lm (whole
+ * segments, else RLK_ERR_CONTRACT). hidden, targets, rms_gamma, lse, entropy, grad_logp and
+ * grad_entropy as in rlk_logprob_backward (lse and entropy of the merged forward).
+ * dh_parts: fp32 [(vocab_end - vocab_begin) / (V / S_c)][num_rows][H], required: one partial per
+ * segment of the shard, w.r.t. the LM-head input (the RMSNorm's output with RLK_FLAG_RMSNORM).
+ * grad_W_shard: fp32 [vocab_end - vocab_begin][H] or NULL (RLK_BWD_ACCUMULATE continues it). */
+rlk_status_t rlk_logprob_backward_partials(rlk_logprob_t handle, const void* hidden,
+                                           const void* W_shard, int64_t vocab_begin,
+                                           int64_t vocab_end, const int32_t* targets,
+                                           int64_t num_rows, const void* rms_gamma,
+                                           const float* lse, const float* entropy,
+                                           const float* grad_logp, const float* grad_entropy,
+                                           float* dh_parts, float* grad_W_shard, uint32_t flags,
+                                           int64_t row_chunk, void* workspace,
+                                           size_t workspace_bytes, rlk_stream_t stream);
+
+/* Host-only: workspace bytes of rlk_logprob_backward_merge. */
+rlk_status_t rlk_logprob_backward_merge_workspace_size(const rlk_logprob_config_t* config,
+                                                       int64_t num_rows, size_t* bytes);
+
+/* Merge of every shard's dh partials: dh_parts fp32 [S_c][num_rows][H], segment-major (all
+ * segments of the vocabulary). Writes grad_hidden fp32 [num_rows][H] (through the RMSNorm with
+ * RLK_FLAG_RMSNORM, which needs hidden and rms_gamma) and, with RLK_FLAG_RMSNORM, grad_gamma fp32
+ * [H] (RLK_BWD_ACCUMULATE continues it). */
+rlk_status_t rlk_logprob_backward_merge(rlk_logprob_t handle, const float* dh_parts,
+                                        const void* hidden, const void* rms_gamma,
+                                        int64_t num_rows, float* grad_hidden, float* grad_gamma,
+                                        uint32_t flags, void* workspace, size_t workspace_bytes,
+                                        rlk_stream_t stream);
+
 /* Compiler, flags and target the library was built with. */
 const char* rlk_build_fingerprint(void);
 

@@ -25,6 +25,10 @@ from ._lib import (  # noqa: F401
     rlk_logprob_config_t,
     rlk_logprob_contract_id,
     rlk_logprob_backward,
+    rlk_logprob_backward_merge,
+    rlk_logprob_backward_merge_workspace_size,
+    rlk_logprob_backward_partials,
+    rlk_logprob_backward_partials_workspace_size,
     rlk_logprob_backward_workspace_size,
     rlk_logprob_create,
     rlk_logprob_destroy,
@@ -292,6 +296,94 @@ class Logprob:
                              RLK_BWD_ACCUMULATE if accumulate else 0, row_chunk,
                              workspace.data_ptr(), workspace.numel(), s.cuda_stream)
         out["_workspace"] = workspace
+        return out
+
+    def backward_partials(self, hidden, W_shard, vocab_begin: int, vocab_end: int, targets, lse,
+                          grad_logp, *, entropy=None, grad_entropy=None, gamma=None,
+                          want_W: bool = True, grad_W_shard=None, accumulate: bool = False,
+                          row_chunk: int = 0, stream=None) -> dict:
+        """One vocab shard's backward: "dh_parts" fp32 [segments of the shard, T, H] and
+        "grad_W_shard" fp32 [vocab_end - vocab_begin, H]."""
+        import torch
+
+        bf = (torch.bfloat16, torch.int16, torch.uint16)
+        H = self.config.hidden_size
+        T = self._targets(targets)
+        # validates the range (segment boundaries) before any shape is derived from it
+        need = rlk_logprob_backward_partials_workspace_size(self.config, T, vocab_begin,
+                                                            vocab_end, row_chunk)
+        self._check(hidden, bf, "hidden", (T, H))
+        self._check(W_shard, bf, "W_shard", (vocab_end - vocab_begin, H))
+        self._check(lse, (torch.float32,), "lse", (T,))
+        self._check(grad_logp, (torch.float32,), "grad_logp", (T,))
+        if grad_entropy is not None:
+            self._check(grad_entropy, (torch.float32,), "grad_entropy", (T,))
+            if entropy is None:
+                raise ValueError("grad_entropy needs the forward's entropy")
+        if entropy is not None:
+            self._check(entropy, (torch.float32,), "entropy", (T,))
+        self._gamma(gamma)
+        dev = torch.device("cuda", self.device)
+        seg_len = self.config.vocab_size // self.config.vocab_segments
+        nloc = (vocab_end - vocab_begin) // seg_len
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        out = {"dh_parts": torch.empty((nloc, T, H), dtype=torch.float32, device=dev)}
+        if want_W:
+            if grad_W_shard is None:
+                if accumulate:
+                    raise ValueError("accumulate=True needs grad_W_shard")
+                grad_W_shard = torch.empty((vocab_end - vocab_begin, H), dtype=torch.float32,
+                                           device=dev)
+            else:
+                self._check(grad_W_shard, (torch.float32,), "grad_W_shard",
+                            (vocab_end - vocab_begin, H))
+            out["grad_W_shard"] = grad_W_shard
+        s = stream if stream is not None else torch.cuda.current_stream(dev)
+        rlk_logprob_backward_partials(self.handle, hidden.data_ptr(), W_shard.data_ptr(),
+                                      vocab_begin, vocab_end, targets.data_ptr(), T, _ptr(gamma),
+                                      lse.data_ptr(), _ptr(entropy), grad_logp.data_ptr(),
+                                      _ptr(grad_entropy), out["dh_parts"].data_ptr(),
+                                      _ptr(out.get("grad_W_shard")),
+                                      RLK_BWD_ACCUMULATE if accumulate else 0, row_chunk,
+                                      ws.data_ptr(), ws.numel(), s.cuda_stream)
+        out["_workspace"] = ws
+        return out
+
+    def backward_merge(self, dh_parts, *, hidden=None, gamma=None, want_gamma: bool | None = None,
+                       grad_gamma=None, accumulate: bool = False, stream=None) -> dict:
+        """Merge of every shard's dh partials ([S_c, T, H] fp32) into "grad_hidden" (and
+        "grad_gamma" with the RMSNorm, which needs the hidden rows and gamma)."""
+        import torch
+
+        H = self.config.hidden_size
+        S = self.config.vocab_segments
+        self._check(dh_parts, (torch.float32,), "dh_parts")
+        if dh_parts.dim() != 3 or dh_parts.shape[0] != S or dh_parts.shape[2] != H:
+            raise ValueError(f"dh_parts must be [{S}, T, {H}]")
+        T = dh_parts.shape[1]
+        if hidden is not None:
+            self._check(hidden, (torch.bfloat16, torch.int16, torch.uint16), "hidden", (T, H))
+        self._gamma(gamma)
+        if want_gamma is None:
+            want_gamma = self.rmsnorm
+        dev = torch.device("cuda", self.device)
+        need = rlk_logprob_backward_merge_workspace_size(self.config, T)
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        out = {"grad_hidden": torch.empty((T, H), dtype=torch.float32, device=dev)}
+        if want_gamma:
+            if grad_gamma is None:
+                if accumulate:
+                    raise ValueError("accumulate=True needs grad_gamma")
+                grad_gamma = torch.empty((H,), dtype=torch.float32, device=dev)
+            else:
+                self._check(grad_gamma, (torch.float32,), "grad_gamma", (H,))
+            out["grad_gamma"] = grad_gamma
+        s = stream if stream is not None else torch.cuda.current_stream(dev)
+        rlk_logprob_backward_merge(self.handle, dh_parts.data_ptr(), _ptr(hidden), _ptr(gamma), T,
+                                   out["grad_hidden"].data_ptr(), _ptr(out.get("grad_gamma")),
+                                   RLK_BWD_ACCUMULATE if accumulate else 0, ws.data_ptr(),
+                                   ws.numel(), s.cuda_stream)
+        out["_workspace"] = ws
         return out
 
     def merge(self, records, targets, *, status=None, stream=None) -> dict:

@@ -91,6 +91,19 @@ _SIGS = {
                                                   ctypes.POINTER(ctypes.c_size_t)]),
     "rlk_logprob_backward": (_ST, [_H, _P, _P, _P, ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P, _P,
                                    ctypes.c_uint32, ctypes.c_int64, _P, ctypes.c_size_t, _S]),
+    "rlk_logprob_backward_partials_workspace_size": (_ST, [ctypes.POINTER(rlk_logprob_config_t),
+                                                           ctypes.c_int64, ctypes.c_int64,
+                                                           ctypes.c_int64, ctypes.c_int64,
+                                                           ctypes.POINTER(ctypes.c_size_t)]),
+    "rlk_logprob_backward_partials": (_ST, [_H, _P, _P, ctypes.c_int64, ctypes.c_int64, _P,
+                                            ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P,
+                                            ctypes.c_uint32, ctypes.c_int64, _P, ctypes.c_size_t,
+                                            _S]),
+    "rlk_logprob_backward_merge_workspace_size": (_ST, [ctypes.POINTER(rlk_logprob_config_t),
+                                                        ctypes.c_int64,
+                                                        ctypes.POINTER(ctypes.c_size_t)]),
+    "rlk_logprob_backward_merge": (_ST, [_H, _P, _P, _P, ctypes.c_int64, _P, _P, ctypes.c_uint32,
+                                         _P, ctypes.c_size_t, _S]),
     "rlk_logprob_contract_id": (ctypes.c_char_p, [_H]),
     "rlk_build_fingerprint": (ctypes.c_char_p, []),
     "rlk_status_string": (ctypes.c_char_p, [_ST]),
@@ -225,6 +238,44 @@ def rlk_logprob_backward(handle, hidden, W_lm, targets, num_rows, rms_gamma, lse
                                       entropy, grad_logp, grad_entropy, grad_hidden, grad_W,
                                       grad_gamma, flags, row_chunk, workspace, workspace_bytes,
                                       stream), "rlk_logprob_backward")
+
+
+def rlk_logprob_backward_partials_workspace_size(config: rlk_logprob_config_t, num_rows: int,
+                                                 vocab_begin: int, vocab_end: int,
+                                                 row_chunk: int) -> int:
+    n = ctypes.c_size_t()
+    check(load().rlk_logprob_backward_partials_workspace_size(ctypes.byref(config), num_rows,
+                                                              vocab_begin, vocab_end, row_chunk,
+                                                              ctypes.byref(n)),
+          "rlk_logprob_backward_partials_workspace_size")
+    return n.value
+
+
+def rlk_logprob_backward_partials(handle, hidden, W_shard, vocab_begin, vocab_end, targets,
+                                  num_rows, rms_gamma, lse, entropy, grad_logp, grad_entropy,
+                                  dh_parts, grad_W_shard, flags, row_chunk, workspace,
+                                  workspace_bytes, stream) -> None:
+    check(load().rlk_logprob_backward_partials(handle, hidden, W_shard, vocab_begin, vocab_end,
+                                               targets, num_rows, rms_gamma, lse, entropy,
+                                               grad_logp, grad_entropy, dh_parts, grad_W_shard,
+                                               flags, row_chunk, workspace, workspace_bytes,
+                                               stream), "rlk_logprob_backward_partials")
+
+
+def rlk_logprob_backward_merge_workspace_size(config: rlk_logprob_config_t, num_rows: int) -> int:
+    n = ctypes.c_size_t()
+    check(load().rlk_logprob_backward_merge_workspace_size(ctypes.byref(config), num_rows,
+                                                           ctypes.byref(n)),
+          "rlk_logprob_backward_merge_workspace_size")
+    return n.value
+
+
+def rlk_logprob_backward_merge(handle, dh_parts, hidden, rms_gamma, num_rows, grad_hidden,
+                               grad_gamma, flags, workspace, workspace_bytes, stream) -> None:
+    check(load().rlk_logprob_backward_merge(handle, dh_parts, hidden, rms_gamma, num_rows,
+                                            grad_hidden, grad_gamma, flags, workspace,
+                                            workspace_bytes, stream),
+          "rlk_logprob_backward_merge")
 
 
 def rlk_logprob_contract_id(handle) -> str:

@@ -301,7 +301,7 @@ __global__ void __launch_bounds__(64 * kGWaves) k_gemm(const GemmArgs a) {
       const uint32_t col0 = cb + 16 * i;
       const uint32_t sg = col0 / Lp;
       const uint32_t c0 = col0 - sg * Lp;  // position inside the segment
-      const int v0 = (int)(sg * L + c0);   // vocab index of col0 when c0 < L
+      const int v0 = (int)(a.v_base + sg * L + c0);  // vocab index of col0 when c0 < L
       const bool col_ok = (int)col0 < a.M;
       static_for<kGNB16>([&](auto jc) {
         constexpr int j = decltype(jc)::value;

@@ -635,11 +635,13 @@ int64_t bwd_chunk(int64_t rows, int64_t row_chunk, int64_t J) {
 }
 
 // want_h: a gradient w.r.t. the LM-head input is needed (grad_hidden, or grad_gamma through the
-// RMSNorm).
-BwdMap bwd_map(const rlk_logprob_config_t& c, int64_t rows, int64_t row_chunk, bool want_h) {
+// RMSNorm); nseg: the vocab segments processed (all of them, or a shard's); shard: the dh
+// partials go to the caller (no tree, no RMSNorm backward here).
+BwdMap bwd_map(const rlk_logprob_config_t& c, int64_t rows, int64_t row_chunk, bool want_h,
+               int nseg = 0, bool shard = false) {
   BwdMap m;
-  const int S = c.vocab_segments;
-  m.L = c.vocab_size / S;
+  const int S = nseg > 0 ? nseg : c.vocab_segments;
+  m.L = c.vocab_size / c.vocab_segments;
   m.Lp = (int64_t)round_up((size_t)m.L, rlk::kBwdKPad);
   m.J = S * m.Lp;
   m.chunk = bwd_chunk(rows, row_chunk, m.J);
@@ -651,13 +653,13 @@ BwdMap bwd_map(const rlk_logprob_config_t& c, int64_t rows, int64_t row_chunk, b
     return at;
   };
   m.dz = take((size_t)m.chunk * (size_t)m.J * 2);
-  m.dpart = (want_h && S > 1) ? take((size_t)S * (size_t)m.chunk * H * 4) : 0;
+  m.dpart = (want_h && S > 1 && !shard) ? take((size_t)S * (size_t)m.chunk * H * 4) : 0;
   const bool rms = c.flags & RLK_FLAG_RMSNORM;
+  const bool rms_bwd = rms && want_h && !shard;
   m.y = rms ? take((size_t)m.chunk * H * 2) : 0;
-  m.dy = (rms && want_h) ? take((size_t)m.chunk * H * 4) : 0;
-  m.r = (rms && want_h) ? take((size_t)m.chunk * 4) : 0;
-  m.gp = (rms && want_h) ? take((size_t)((m.chunk + rlk::kGammaGroup - 1) / rlk::kGammaGroup) * H * 4)
-                         : 0;
+  m.dy = rms_bwd ? take((size_t)m.chunk * H * 4) : 0;
+  m.r = rms_bwd ? take((size_t)m.chunk * 4) : 0;
+  m.gp = rms_bwd ? take((size_t)((m.chunk + rlk::kGammaGroup - 1) / rlk::kGammaGroup) * H * 4) : 0;
   m.total = std::max<size_t>(off, 256);
   return m;
 }
@@ -675,6 +677,190 @@ rlk_status_t check_bwd_rows(const rlk_logprob_config_t& c, int64_t num_rows, int
       (int64_t)rlk::kBwdKPad * m.J * 2 >= 0x7fffffffLL)
     return fail(RLK_ERR_UNSUPPORTED_SHAPE, "vocab segment x hidden size too large for the backward");
   return RLK_OK;
+}
+
+// Arguments of one backward run over the vocab segments [s0, s1) (all of them, or a shard's).
+struct BwdRun {
+  const uint16_t* hidden;
+  const uint16_t* W;  // W_lm rows from s0 L on
+  int s0, s1;
+  const int32_t* targets;
+  int64_t T;
+  const uint16_t* gamma;
+  const float *lse, *entropy, *g, *gH;
+  float* grad_hidden;  // full run only
+  float* grad_W;       // rows of the range
+  float* grad_gamma;   // full run only
+  float* parts;        // shard run: per-segment dh partials [s1 - s0][T][H]
+  bool accumulate;
+  int64_t row_chunk;
+};
+
+rlk_status_t backward_run(const rlk_logprob* h, const BwdRun& b, void* workspace,
+                            size_t workspace_bytes, hipStream_t s) {
+  const rlk_logprob_config_t& c = h->cfg;
+  const int64_t num_rows = b.T;
+  const bool rms = c.flags & RLK_FLAG_RMSNORM;
+  const bool shard = b.parts != nullptr;
+  const bool want_x = b.grad_hidden != nullptr, want_w = b.grad_W != nullptr;
+  const bool want_g = b.grad_gamma != nullptr;
+  const bool want_h = want_x || want_g || shard;
+  const int nseg = b.s1 - b.s0;
+  const BwdMap m = bwd_map(c, num_rows, b.row_chunk, want_h, nseg, shard);
+  if (!workspace || workspace_bytes < m.total)
+    return fail(RLK_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", m.total,
+                workspace_bytes);
+  DeviceGuard guard(h->device);
+  if (guard.err != hipSuccess) return hip_fail(guard.err, "hipSetDevice");
+  const bool accumulate = b.accumulate;
+  const int S = nseg;
+  const int H = c.hidden_size;
+  const int64_t Vr = (int64_t)nseg * m.L;  // vocab rows of the range (of W_lm or the shard)
+  float* const grad_W = b.grad_W;
+  float* const grad_gamma = b.grad_gamma;
+  float* const grad_hidden = b.grad_hidden;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  hipError_t e;
+  if (num_rows == 0) {
+    if (want_w && !accumulate) {
+      e = rlk::launch_zero_f32(grad_W, Vr * H, s);
+      if (e != hipSuccess) return hip_fail(e, "zero launch");
+    }
+    if (want_g && !accumulate) {
+      e = rlk::launch_zero_f32(grad_gamma, H, s);
+      if (e != hipSuccess) return hip_fail(e, "zero launch");
+    }
+    return ok();
+  }
+  uint16_t* dz = reinterpret_cast<uint16_t*>(ws + m.dz);
+  float* dpart = reinterpret_cast<float*>(ws + m.dpart);
+  uint16_t* ynorm = reinterpret_cast<uint16_t*>(ws + m.y);
+  float* dy = reinterpret_cast<float*>(ws + m.dy);
+  float* rrow = reinterpret_cast<float*>(ws + m.r);
+  float* gpart = reinterpret_cast<float*>(ws + m.gp);
+  const uint16_t* gam = b.gamma;
+  const uint16_t* hid = b.hidden;
+  const uint16_t* Wb = b.W;
+  int64_t chunk_no = 0;
+  for (int64_t r0 = 0; r0 < num_rows; r0 += m.chunk, ++chunk_no) {
+    const int64_t r1 = std::min<int64_t>(num_rows, r0 + m.chunk);
+    const int64_t n = r1 - r0;
+    const int64_t np = (int64_t)round_up((size_t)n, rlk::kBwdKPad);
+    // the LM-head input of these rows: the hidden rows, or their RMSNorm (C12, recomputed)
+    const uint16_t* hin = hid + r0 * H;
+    if (rms) {
+      rlk::RmsArgs ra;
+      ra.x = hin;
+      ra.gamma = gam;
+      ra.y = ynorm;
+      ra.rows = (int32_t)n;
+      ra.H = H;
+      ra.inv_H = 1.0f / (float)H;
+      ra.eps = c.rms_eps;
+      ra.portable = (c.flags & RLK_FLAG_PORTABLE_EXP) ? 1 : 0;
+      e = rlk::launch_rmsnorm(ra, s);
+      if (e != hipSuccess) return hip_fail(e, "rmsnorm launch");
+      hin = ynorm;
+    }
+    // B1: dz over the segment-padded positions (it writes the padding zeros)
+    rlk::GemmArgs a{};
+    a.A = Wb;
+    a.lda = H;
+    a.B = hin;
+    a.ldb = H;
+    a.M = (int32_t)m.J;
+    a.N = (int32_t)n;
+    a.K = H;
+    a.seg_len = m.L;
+    a.seg_pad = m.Lp;
+    a.targets = b.targets + r0;
+    a.lse = b.lse + r0;
+    a.ent = b.gH ? b.entropy + r0 : nullptr;
+    a.g = b.g + r0;
+    a.gH = b.gH ? b.gH + r0 : nullptr;
+    a.dz = dz;
+    a.lddz = m.J;
+    a.v_base = (int64_t)b.s0 * m.L;
+    a.inv_tau = c.inv_temperature;
+    a.portable = (c.flags & RLK_FLAG_PORTABLE_EXP) ? 1 : 0;
+    e = rlk::launch_gemm_dz(a, s);
+    if (e != hipSuccess) return hip_fail(e, "dz launch");
+    if (want_h) {
+      // B2: per segment one chain over its positions (W read K-major, rows past the segment read
+      // as zeros), then the segment tree
+      rlk::GemmArgs g{};
+      g.A = Wb;
+      g.lda = H;
+      g.a_batch = m.L * H;
+      g.ka_rows = m.L;
+      g.B = dz;
+      g.ldb = m.J;
+      g.b_batch = m.Lp;
+      g.M = H;
+      g.N = (int32_t)n;
+      g.K = (int32_t)m.Lp;
+      float* dh = rms ? dy : grad_hidden + r0 * H;
+      if (shard) {
+        // a shard's per-segment partials, before the tree: parts[s - s0][t][k]
+        g.C = b.parts + r0 * H;
+        g.c_batch = num_rows * H;
+      } else {
+        g.C = S > 1 ? dpart : dh;
+        g.c_batch = n * H;
+      }
+      g.ldc = H;
+      e = rlk::launch_gemm_out(g, S, false, s);
+      if (e != hipSuccess) return hip_fail(e, "dh launch");
+      if (S > 1 && !shard) {
+        e = rlk::launch_seg_tree(dpart, n * H, S, dh, n * H, s);
+        if (e != hipSuccess) return hip_fail(e, "dh tree launch");
+      }
+      if (rms && !shard) {
+        // B4: through the RMSNorm to its input, and the gamma gradient
+        rlk::RmsBwdArgs rb;
+        rb.x = hid + r0 * H;
+        rb.gamma = gam;
+        rb.dy = dy;
+        rb.dx = want_x ? grad_hidden + r0 * H : nullptr;
+        rb.r = rrow;
+        rb.rows = (int32_t)n;
+        rb.H = H;
+        rb.inv_H = 1.0f / (float)H;
+        rb.eps = c.rms_eps;
+        rb.portable = (c.flags & RLK_FLAG_PORTABLE_EXP) ? 1 : 0;
+        e = rlk::launch_rmsnorm_bwd(rb, s);
+        if (e != hipSuccess) return hip_fail(e, "rmsnorm backward launch");
+        if (want_g) {
+          e = rlk::launch_dgamma(dy, hid + r0 * H, rrow, gpart, (int)n, H, grad_gamma,
+                                 accumulate || chunk_no > 0, s);
+          if (e != hipSuccess) return hip_fail(e, "dgamma launch");
+        }
+      }
+    }
+    if (want_w) {
+      // B3: the hidden rows and dz read K-major (K = row, rows past the chunk read as zeros);
+      // the chain over rows continues from the previous chunk
+      rlk::GemmArgs g{};
+      g.A = hin;
+      g.lda = H;
+      g.ka_rows = n;
+      g.B = dz;
+      g.ldb = m.J;
+      g.kb_rows = n;
+      g.M = H;
+      g.N = (int32_t)m.J;
+      g.K = (int32_t)np;
+      g.seg_len = m.L;
+      g.seg_pad = m.Lp;
+      g.C = grad_W;
+      g.ldc = H;
+      g.accumulate = (accumulate || chunk_no > 0) ? 1 : 0;
+      g.map_rows = 1;
+      e = rlk::launch_gemm_out(g, 1, true, s);
+      if (e != hipSuccess) return hip_fail(e, "dW launch");
+    }
+  }
+  return ok();
 }
 
 }  // namespace
@@ -726,150 +912,213 @@ RLK_API rlk_status_t rlk_logprob_backward(rlk_logprob_t h, const void* hidden, c
       !aligned16(grad_hidden) || !aligned16(grad_W) || !aligned16(workspace) ||
       !aligned16(rms_gamma) || !aligned16(grad_gamma))
     return fail(RLK_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
-  const BwdMap m = bwd_map(c, num_rows, row_chunk, want_h);
+  BwdRun b;
+  b.hidden = static_cast<const uint16_t*>(hidden);
+  b.W = static_cast<const uint16_t*>(W_lm);
+  b.s0 = 0;
+  b.s1 = c.vocab_segments;
+  b.targets = targets;
+  b.T = num_rows;
+  b.gamma = static_cast<const uint16_t*>(rms_gamma);
+  b.lse = lse;
+  b.entropy = entropy;
+  b.g = grad_logp;
+  b.gH = grad_entropy;
+  b.grad_hidden = grad_hidden;
+  b.grad_W = grad_W;
+  b.grad_gamma = grad_gamma;
+  b.parts = nullptr;
+  b.accumulate = flags & RLK_BWD_ACCUMULATE;
+  b.row_chunk = row_chunk;
+  return backward_run(h, b, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+// ---- the backward of one vocab shard, and the merge of the shards' dh partials ----
+namespace {
+
+rlk_status_t check_shard_range(const rlk_logprob_config_t& c, int64_t vocab_begin,
+                               int64_t vocab_end, int* s0, int* s1) {
+  const Geometry g = geometry(c);
+  if (vocab_begin < 0 || vocab_end > c.vocab_size || vocab_end <= vocab_begin ||
+      vocab_begin % g.seg_len != 0 || vocab_end % g.seg_len != 0)
+    return fail(RLK_ERR_CONTRACT, "vocab range [%lld, %lld) is not on segment boundaries of %lld",
+                (long long)vocab_begin, (long long)vocab_end, (long long)g.seg_len);
+  *s0 = (int)(vocab_begin / g.seg_len);
+  *s1 = (int)(vocab_end / g.seg_len);
+  return RLK_OK;
+}
+
+// merge workspace: dy [T][H] fp32, r [T], dgamma group sums (RMSNorm only)
+struct MergeMap {
+  size_t dy, r, gp, total;
+};
+MergeMap merge_map(const rlk_logprob_config_t& c, int64_t rows) {
+  MergeMap m{};
+  const size_t H = (size_t)c.hidden_size;
+  const size_t T = (size_t)std::max<int64_t>(rows, 1);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = round_up(off + bytes, 256);
+    return at;
+  };
+  if (c.flags & RLK_FLAG_RMSNORM) {
+    m.dy = take(T * H * 4);
+    m.r = take(T * 4);
+    m.gp = take((T + rlk::kGammaGroup - 1) / rlk::kGammaGroup * H * 4);
+  }
+  m.total = std::max<size_t>(off, 256);
+  return m;
+}
+
+}  // namespace
+
+RLK_API rlk_status_t rlk_logprob_backward_partials_workspace_size(
+    const rlk_logprob_config_t* config, int64_t num_rows, int64_t vocab_begin, int64_t vocab_end,
+    int64_t row_chunk, size_t* bytes) {
+  if (!bytes) return fail(RLK_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  rlk_status_t st = check_config(config);
+  if (st != RLK_OK) return st;
+  st = check_bwd_rows(*config, num_rows, row_chunk);
+  if (st != RLK_OK) return st;
+  int s0, s1;
+  st = check_shard_range(*config, vocab_begin, vocab_end, &s0, &s1);
+  if (st != RLK_OK) return st;
+  *bytes = bwd_map(*config, num_rows, row_chunk, true, s1 - s0, true).total;
+  return ok();
+}
+
+RLK_API rlk_status_t rlk_logprob_backward_partials(
+    rlk_logprob_t h, const void* hidden, const void* W_shard, int64_t vocab_begin,
+    int64_t vocab_end, const int32_t* targets, int64_t num_rows, const void* rms_gamma,
+    const float* lse, const float* entropy, const float* grad_logp, const float* grad_entropy,
+    float* dh_parts, float* grad_W_shard, uint32_t flags, int64_t row_chunk, void* workspace,
+    size_t workspace_bytes, rlk_stream_t stream) {
+  if (!h) return fail(RLK_ERR_INVALID_ARGUMENT, "handle is NULL");
+  const rlk_logprob_config_t& c = h->cfg;
+  if (flags & ~RLK_BWD_ACCUMULATE)
+    return fail(RLK_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", flags);
+  rlk_status_t st = check_bwd_rows(c, num_rows, row_chunk);
+  if (st != RLK_OK) return st;
+  int s0, s1;
+  st = check_shard_range(c, vocab_begin, vocab_end, &s0, &s1);
+  if (st != RLK_OK) return st;
+  const bool rms = c.flags & RLK_FLAG_RMSNORM;
+  if (!rms && rms_gamma)
+    return fail(RLK_ERR_CONTRACT, "rms_gamma given but RLK_FLAG_RMSNORM not set");
+  if (rms && num_rows > 0 && !rms_gamma)
+    return fail(RLK_ERR_INVALID_ARGUMENT, "rms_gamma is required with RLK_FLAG_RMSNORM");
+  if (!dh_parts) return fail(RLK_ERR_INVALID_ARGUMENT, "dh_parts is required");
+  if (grad_entropy && !(c.flags & RLK_FLAG_ENTROPY))
+    return fail(RLK_ERR_CONTRACT, "grad_entropy given but RLK_FLAG_ENTROPY not set");
+  if (grad_entropy && !entropy)
+    return fail(RLK_ERR_INVALID_ARGUMENT, "grad_entropy needs the forward's entropy");
+  if (num_rows > 0 && (!hidden || !W_shard || !targets || !lse || !grad_logp))
+    return fail(RLK_ERR_INVALID_ARGUMENT, "hidden, W_shard, targets, lse and grad_logp are required");
+  if (!aligned16(hidden) || !aligned16(W_shard) || !aligned16(targets) || !aligned16(lse) ||
+      !aligned16(grad_logp) || !aligned16(entropy) || !aligned16(grad_entropy) ||
+      !aligned16(dh_parts) || !aligned16(grad_W_shard) || !aligned16(workspace) ||
+      !aligned16(rms_gamma))
+    return fail(RLK_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
+  if (num_rows == 0) return ok();
+  BwdRun b;
+  b.hidden = static_cast<const uint16_t*>(hidden);
+  b.W = static_cast<const uint16_t*>(W_shard);
+  b.s0 = s0;
+  b.s1 = s1;
+  b.targets = targets;
+  b.T = num_rows;
+  b.gamma = static_cast<const uint16_t*>(rms_gamma);
+  b.lse = lse;
+  b.entropy = entropy;
+  b.g = grad_logp;
+  b.gH = grad_entropy;
+  b.grad_hidden = nullptr;
+  b.grad_W = grad_W_shard;
+  b.grad_gamma = nullptr;
+  b.parts = dh_parts;
+  b.accumulate = flags & RLK_BWD_ACCUMULATE;
+  b.row_chunk = row_chunk;
+  return backward_run(h, b, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+RLK_API rlk_status_t rlk_logprob_backward_merge_workspace_size(const rlk_logprob_config_t* config,
+                                                               int64_t num_rows, size_t* bytes) {
+  if (!bytes) return fail(RLK_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  rlk_status_t st = check_config(config);
+  if (st != RLK_OK) return st;
+  if (num_rows < 0 || num_rows > 0x7fffffffLL)
+    return fail(RLK_ERR_INVALID_ARGUMENT, "num_rows out of range");
+  *bytes = merge_map(*config, num_rows).total;
+  return ok();
+}
+
+RLK_API rlk_status_t rlk_logprob_backward_merge(rlk_logprob_t h, const float* dh_parts,
+                                                const void* hidden, const void* rms_gamma,
+                                                int64_t num_rows, float* grad_hidden,
+                                                float* grad_gamma, uint32_t flags,
+                                                void* workspace, size_t workspace_bytes,
+                                                rlk_stream_t stream) {
+  if (!h) return fail(RLK_ERR_INVALID_ARGUMENT, "handle is NULL");
+  const rlk_logprob_config_t& c = h->cfg;
+  if (flags & ~RLK_BWD_ACCUMULATE)
+    return fail(RLK_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", flags);
+  if (num_rows < 0 || num_rows > 0x7fffffffLL)
+    return fail(RLK_ERR_INVALID_ARGUMENT, "num_rows out of range");
+  const bool rms = c.flags & RLK_FLAG_RMSNORM;
+  if (!rms && (rms_gamma || grad_gamma))
+    return fail(RLK_ERR_CONTRACT, "rms_gamma / grad_gamma given but RLK_FLAG_RMSNORM not set");
+  if (rms && num_rows > 0 && (!rms_gamma || !hidden))
+    return fail(RLK_ERR_INVALID_ARGUMENT, "hidden and rms_gamma are required with RLK_FLAG_RMSNORM");
+  if (!grad_hidden && !grad_gamma) return fail(RLK_ERR_INVALID_ARGUMENT, "no gradient requested");
+  if (num_rows > 0 && !dh_parts) return fail(RLK_ERR_INVALID_ARGUMENT, "dh_parts is required");
+  if (!rms && !grad_hidden) return fail(RLK_ERR_INVALID_ARGUMENT, "grad_hidden is required");
+  if (!aligned16(dh_parts) || !aligned16(hidden) || !aligned16(rms_gamma) ||
+      !aligned16(grad_hidden) || !aligned16(grad_gamma) || !aligned16(workspace))
+    return fail(RLK_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
+  const MergeMap m = merge_map(c, num_rows);
   if (!workspace || workspace_bytes < m.total)
     return fail(RLK_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", m.total,
                 workspace_bytes);
   DeviceGuard guard(h->device);
   if (guard.err != hipSuccess) return hip_fail(guard.err, "hipSetDevice");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool accumulate = flags & RLK_BWD_ACCUMULATE;
-  const int S = c.vocab_segments;
   const int H = c.hidden_size;
-  const int64_t V = c.vocab_size;
+  const bool accumulate = flags & RLK_BWD_ACCUMULATE;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   hipError_t e;
   if (num_rows == 0) {
-    if (want_w && !accumulate) {
-      e = rlk::launch_zero_f32(grad_W, V * H, s);
-      if (e != hipSuccess) return hip_fail(e, "zero launch");
-    }
-    if (want_g && !accumulate) {
+    if (grad_gamma && !accumulate) {
       e = rlk::launch_zero_f32(grad_gamma, H, s);
       if (e != hipSuccess) return hip_fail(e, "zero launch");
     }
     return ok();
   }
-  uint16_t* dz = reinterpret_cast<uint16_t*>(ws + m.dz);
-  float* dpart = reinterpret_cast<float*>(ws + m.dpart);
-  uint16_t* ynorm = reinterpret_cast<uint16_t*>(ws + m.y);
-  float* dy = reinterpret_cast<float*>(ws + m.dy);
-  float* rrow = reinterpret_cast<float*>(ws + m.r);
-  float* gpart = reinterpret_cast<float*>(ws + m.gp);
-  const uint16_t* gam = static_cast<const uint16_t*>(rms_gamma);
-  const uint16_t* hid = static_cast<const uint16_t*>(hidden);
-  const uint16_t* Wb = static_cast<const uint16_t*>(W_lm);
-  int64_t chunk_no = 0;
-  for (int64_t r0 = 0; r0 < num_rows; r0 += m.chunk, ++chunk_no) {
-    const int64_t r1 = std::min<int64_t>(num_rows, r0 + m.chunk);
-    const int64_t n = r1 - r0;
-    const int64_t np = (int64_t)round_up((size_t)n, rlk::kBwdKPad);
-    // the LM-head input of these rows: the hidden rows, or their RMSNorm (C12, recomputed)
-    const uint16_t* hin = hid + r0 * H;
-    if (rms) {
-      rlk::RmsArgs ra;
-      ra.x = hin;
-      ra.gamma = gam;
-      ra.y = ynorm;
-      ra.rows = (int32_t)n;
-      ra.H = H;
-      ra.inv_H = 1.0f / (float)H;
-      ra.eps = c.rms_eps;
-      ra.portable = (c.flags & RLK_FLAG_PORTABLE_EXP) ? 1 : 0;
-      e = rlk::launch_rmsnorm(ra, s);
-      if (e != hipSuccess) return hip_fail(e, "rmsnorm launch");
-      hin = ynorm;
-    }
-    // B1: dz over the segment-padded positions (it writes the padding zeros)
-    rlk::GemmArgs a{};
-    a.A = Wb;
-    a.lda = H;
-    a.B = hin;
-    a.ldb = H;
-    a.M = (int32_t)m.J;
-    a.N = (int32_t)n;
-    a.K = H;
-    a.seg_len = m.L;
-    a.seg_pad = m.Lp;
-    a.targets = targets + r0;
-    a.lse = lse + r0;
-    a.ent = grad_entropy ? entropy + r0 : nullptr;
-    a.g = grad_logp + r0;
-    a.gH = grad_entropy ? grad_entropy + r0 : nullptr;
-    a.dz = dz;
-    a.lddz = m.J;
-    a.V = V;
-    a.inv_tau = c.inv_temperature;
-    a.portable = (c.flags & RLK_FLAG_PORTABLE_EXP) ? 1 : 0;
-    e = rlk::launch_gemm_dz(a, s);
-    if (e != hipSuccess) return hip_fail(e, "dz launch");
-    if (want_h) {
-      // B2: per segment one chain over its positions (W read K-major, rows past the segment read
-      // as zeros), then the segment tree
-      rlk::GemmArgs g{};
-      g.A = Wb;
-      g.lda = H;
-      g.a_batch = m.L * H;
-      g.ka_rows = m.L;
-      g.B = dz;
-      g.ldb = m.J;
-      g.b_batch = m.Lp;
-      g.M = H;
-      g.N = (int32_t)n;
-      g.K = (int32_t)m.Lp;
-      float* dh = rms ? dy : grad_hidden + r0 * H;
-      g.C = S > 1 ? dpart : dh;
-      g.ldc = H;
-      g.c_batch = n * H;
-      e = rlk::launch_gemm_out(g, S, false, s);
-      if (e != hipSuccess) return hip_fail(e, "dh launch");
-      if (S > 1) {
-        e = rlk::launch_seg_tree(dpart, n * H, S, dh, n * H, s);
-        if (e != hipSuccess) return hip_fail(e, "dh tree launch");
-      }
-      if (rms) {
-        // B4: through the RMSNorm to its input, and the gamma gradient
-        rlk::RmsBwdArgs rb;
-        rb.x = hid + r0 * H;
-        rb.gamma = gam;
-        rb.dy = dy;
-        rb.dx = want_x ? grad_hidden + r0 * H : nullptr;
-        rb.r = rrow;
-        rb.rows = (int32_t)n;
-        rb.H = H;
-        rb.inv_H = 1.0f / (float)H;
-        rb.eps = c.rms_eps;
-        rb.portable = (c.flags & RLK_FLAG_PORTABLE_EXP) ? 1 : 0;
-        e = rlk::launch_rmsnorm_bwd(rb, s);
-        if (e != hipSuccess) return hip_fail(e, "rmsnorm backward launch");
-        if (want_g) {
-          e = rlk::launch_dgamma(dy, hid + r0 * H, rrow, gpart, (int)n, H, grad_gamma,
-                                 accumulate || chunk_no > 0, s);
-          if (e != hipSuccess) return hip_fail(e, "dgamma launch");
-        }
-      }
-    }
-    if (want_w) {
-      // B3: the hidden rows and dz read K-major (K = row, rows past the chunk read as zeros);
-      // the chain over rows continues from the previous chunk
-      rlk::GemmArgs g{};
-      g.A = hin;
-      g.lda = H;
-      g.ka_rows = n;
-      g.B = dz;
-      g.ldb = m.J;
-      g.kb_rows = n;
-      g.M = H;
-      g.N = (int32_t)m.J;
-      g.K = (int32_t)np;
-      g.seg_len = m.L;
-      g.seg_pad = m.Lp;
-      g.C = grad_W;
-      g.ldc = H;
-      g.accumulate = (accumulate || chunk_no > 0) ? 1 : 0;
-      g.map_rows = 1;
-      e = rlk::launch_gemm_out(g, 1, true, s);
-      if (e != hipSuccess) return hip_fail(e, "dW launch");
+  const int64_t n = num_rows * H;
+  // B2's segment tree (B4 then takes it through the RMSNorm)
+  float* dh = rms ? reinterpret_cast<float*>(ws + m.dy) : grad_hidden;
+  e = rlk::launch_seg_tree(dh_parts, n, c.vocab_segments, dh, n, s);
+  if (e != hipSuccess) return hip_fail(e, "dh tree launch");
+  if (rms) {
+    float* rrow = reinterpret_cast<float*>(ws + m.r);
+    rlk::RmsBwdArgs rb;
+    rb.x = static_cast<const uint16_t*>(hidden);
+    rb.gamma = static_cast<const uint16_t*>(rms_gamma);
+    rb.dy = dh;
+    rb.dx = grad_hidden;
+    rb.r = rrow;
+    rb.rows = (int32_t)num_rows;
+    rb.H = H;
+    rb.inv_H = 1.0f / (float)H;
+    rb.eps = c.rms_eps;
+    rb.portable = (c.flags & RLK_FLAG_PORTABLE_EXP) ? 1 : 0;
+    e = rlk::launch_rmsnorm_bwd(rb, s);
+    if (e != hipSuccess) return hip_fail(e, "rmsnorm backward launch");
+    if (grad_gamma) {
+      e = rlk::launch_dgamma(dh, static_cast<const uint16_t*>(hidden), rrow,
+                             reinterpret_cast<float*>(ws + m.gp), (int)num_rows, H, grad_gamma,
+                             accumulate, s);
+      if (e != hipSuccess) return hip_fail(e, "dgamma launch");
     }
   }
   return ok();

@@ -125,7 +125,7 @@ struct GemmArgs {
   const float* gH;          // dL/dentropy [rows] or null
   uint16_t* dz;             // bf16 [rows][S_c Lp]
   int64_t lddz;
-  int64_t V;
+  int64_t v_base;           // global vocab index of position 0 (a shard's first row)
   float inv_tau;
   int32_t portable;
 };

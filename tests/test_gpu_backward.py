@@ -295,3 +295,37 @@ def test_backward_norm_head_rows_full_width(rlk):
     mx, fro = _rel(got["grad_W"][rw], want["dW"])
     print("grad_W", mx, fro, flush=True)
     assert mx <= 1e-3 and fro <= 1e-4
+
+
+@pytest.mark.parametrize("rms", [False, True])
+def test_backward_vocab_shards_equal_one_pass(rlk, rms):
+    """Shards of 1, 2 and 4 segments (S_c = 4) computing their dh partials and grad_W rows, merged
+    in the segment tree, give the one-pass backward's bits: the vocab-parallel split of B2/B3."""
+    import torch
+
+    T, H, V, S = 200, 256, 3000, 4
+    if rms:
+        x, W, gam, y, g, gH = _rms_inputs(T, H, V, 640, 9)
+        one, (lp, xd, Wd, yd, gd_, fw, gd, gHd) = _run_rms(rlk, x, W, gam, y, g, gH, S=S,
+                                                            tau=0.7)
+    else:
+        h, W, y, g, gH = _inputs(T, H, V, 650, 9)
+        one, (lp, xd, Wd, yd, fw, gd, gHd) = _run(rlk, h, W, y, g, gH, S=S, tau=0.7)
+        gd_ = None
+    ent = fw["entropy"]
+    seg = V // S
+    for cuts in ([0, 4], [0, 2, 4], [0, 1, 2, 3, 4], [0, 1, 4]):
+        say(f"backward shards {cuts} rms={rms}")
+        parts, rows = [], []
+        for a, b in zip(cuts[:-1], cuts[1:]):
+            v0, v1 = a * seg, b * seg
+            o = lp.backward_partials(xd, Wd[v0:v1].contiguous(), v0, v1, yd, fw["lse"], gd,
+                                     entropy=ent, grad_entropy=gHd, gamma=gd_)
+            parts.append(o["dh_parts"])
+            rows.append(o["grad_W_shard"])
+        m = lp.backward_merge(torch.cat(parts), hidden=xd if rms else None, gamma=gd_)
+        torch.cuda.synchronize()
+        assert_bitwise(m["grad_hidden"], one["grad_hidden"], f"dh {cuts}")
+        assert_bitwise(torch.cat(rows), one["grad_W"], f"dW {cuts}")
+        if rms:
+            assert_bitwise(m["grad_gamma"], one["grad_gamma"], f"dgamma {cuts}")
