@@ -14,6 +14,7 @@ oracle timed on a bounded sample of the same rows.
     python bench.py [--steps K] [--warmup W] [--gpus 1]
     python bench.py --copy-calibration-mib 1024   # a plain device copy, for PMC byte scaling
     python bench.py --pmc-summary DIR             # profiles/ summaries from rocprofv3 output
+    python bench.py --backward-only --steps 5     # the backward alone (for its kernel summary)
 
 The PMC summary (profiles/lmhead_qwen3_8b_head_pmc.txt) is written from five rocprofv3 runs of
 this script, each into its own folder under DIR (the commands are printed into the summary):
@@ -489,6 +490,8 @@ def main() -> int:
                     help="write the profiles/ summaries from the rocprofv3 runs under DIR")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the rollout-layout and norm_head measurements")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="time only the backward of the workload (for its rocprofv3 summary)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -524,6 +527,10 @@ def main() -> int:
     Wd = torch.from_numpy(Wb.view(np.int16)).to(dev)
     yd = torch.from_numpy(y.astype(np.int32)).to(dev)
     gd = None if gamma is None else torch.from_numpy(gamma.view(np.int16)).to(dev)
+    if args.backward_only:
+        r = backward(rlk, np, torch, hd, Wd, yd, w, steps=args.steps, warmup=args.warmup)
+        print(json.dumps({"what": "backward", "workload": args.workload, **r}), flush=True)
+        return 0
     lp = rlk.Logprob(w.H, w.V, vocab_segments=w.segments, temperature=w.tau, rmsnorm=w.rmsnorm,
                      rms_eps=w.rms_eps, entropy=w.rmsnorm, device=0)
     layout, keep = rlk.make_layout(w.T)

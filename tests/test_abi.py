@@ -178,3 +178,18 @@ def test_backward_workspace_size(lib):
         assert e.value.status in (_lib.RLK_ERR_UNSUPPORTED_SHAPE, _lib.RLK_ERR_INVALID_ARGUMENT)
     with pytest.raises(_lib.RlkError):
         _lib.rlk_logprob_backward_workspace_size(cfg, -1, 0)
+
+
+def test_backward_shard_workspace_sizes(lib):
+    cfg = make_config(256, 1000, vocab_segments=4)  # segments of 250 (padded to 256)
+    n = _lib.rlk_logprob_backward_partials_workspace_size(cfg, 64, 250, 750, 0)
+    assert n >= 64 * 2 * 256 * 2  # dz for the shard's 2 segments
+    full = _lib.rlk_logprob_backward_workspace_size(cfg, 64, 0)
+    assert n < full  # no tree partials, half the positions
+    for lo, hi in ((0, 100), (250, 251), (-250, 250), (750, 1250), (500, 500)):
+        with pytest.raises(_lib.RlkError) as e:
+            _lib.rlk_logprob_backward_partials_workspace_size(cfg, 64, lo, hi, 0)
+        assert e.value.status == _lib.RLK_ERR_CONTRACT
+    assert _lib.rlk_logprob_backward_merge_workspace_size(cfg, 64) == 256
+    rms = make_config(256, 1000, rmsnorm=True)
+    assert _lib.rlk_logprob_backward_merge_workspace_size(rms, 64) >= 64 * 256 * 4

@@ -163,6 +163,11 @@ def test_backward_refusals(rlk):
         lp.backward(hd, Wd, yd, lse, gd, row_chunk=100)
     with pytest.raises(ValueError):
         lp.backward(hd, Wd, yd, lse[:4], gd)
+    lp4 = rlk.Logprob(H, V, vocab_segments=4)
+    with pytest.raises(rlk.RlkError):  # a shard must be whole segments (of 250 here)
+        lp4.backward_partials(hd, Wd[:300].contiguous(), 0, 300, yd, lse, gd)
+    with pytest.raises(ValueError):  # the merge takes every segment's partial
+        lp4.backward_merge(torch.zeros((2, 8, H), dtype=torch.float32, device="cuda"))
 
 
 def test_backward_full_size_sampled(rlk):
