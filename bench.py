@@ -17,7 +17,8 @@ oracle timed on a bounded sample of the same rows.
     python bench.py --backward-only --steps 5     # the backward alone (for its kernel summary)
 
 The PMC summary (profiles/lmhead_qwen3_8b_head_pmc.txt) is written from five rocprofv3 runs of
-this script, each into its own folder under DIR (the commands are printed into the summary):
+this script, each into its own folder under DIR (the commands are printed into the summary), and
+the backward's kernel summary from a sixth (bwd: --kernel-trace --stats, --backward-only):
   stats   --kernel-trace --stats, default step counts     (kernel durations)
   fetch   --pmc FETCH_SIZE GRBM_GUI_ACTIVE --kernel-trace (bytes read from HBM/MALL, clock)
   write   --pmc WRITE_SIZE SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE --kernel-trace
@@ -46,9 +47,11 @@ METRIC = "selected-token logprobs/sec at H=4096,V=151936; MFMA util; layout mism
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "lmhead_qwen3_8b_head_pmc.txt")
 PROFILE_STATS = os.path.join(ROOT, "profiles", "lmhead_qwen3_8b_head_kernel_stats.txt")
+PROFILE_BWD_STATS = os.path.join(ROOT, "profiles", "backward_qwen3_8b_head_kernel_stats.txt")
 NOMINAL_SCLK_MHZ = 2400.0  # the clock the published MFMA peak is quoted at
 PROF_ARGS = "--steps 3 --warmup 1 --no-cpu-baseline --no-layout-check --no-extras"
 STATS_ARGS = "--steps 30 --warmup 3 --no-cpu-baseline --no-layout-check --no-extras"
+BWD_ARGS = "--backward-only --steps 5 --warmup 2"
 # the sources the LM-head kernel is compiled from (its file, the shared K loop and primitives,
 # the argument structs): a change to any of them makes the committed PMC figures stale
 KERNEL_SRCS = [os.path.join(ROOT, "invariant_lm_head_deterministic_amd", "csrc", f)
@@ -161,6 +164,7 @@ def write_pmc_summary(base: str) -> None:
                   PROF_ARGS),
         "cfetch": ("--pmc FETCH_SIZE", "--copy-calibration-mib 1024"),
         "cwrite": ("--pmc WRITE_SIZE", "--copy-calibration-mib 1024"),
+        "bwd": ("--kernel-trace --stats", BWD_ARGS),
     }
     cmds = {k: cmd.format(opts=o, d=os.path.join(base, k), args=a) for k, (o, a) in runs.items()}
     mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
@@ -221,6 +225,18 @@ bf16_peak_at_sclk_tflops: {PEAK_BF16_TFLOPS * sclk / NOMINAL_SCLK_MHZ:.0f}
     with open(PROFILE_STATS, "w") as f:
         f.write(head + stats)
     print(head + stats)
+    if os.path.isdir(os.path.join(base, "bwd")):
+        bstats = open(_one(os.path.join(base, "bwd"), "kernel_stats.csv")).read()
+        bhead = f"""# Kernel durations of the backward, qwen3_8b_head workload (T=4096, H=4096, V=151936,
+# 4 vocab segments): per step one dz GEMM (k_gemm<0,...>), one dh GEMM over the 4 segments
+# (k_gemm<1,...,true,false>), the segment tree, one dW GEMM (k_gemm<1,...,true,true>)
+# command (from the repository root, TMPDIR=/tmp):
+#   {cmds["bwd"]}
+# (run_kernel_stats.csv, durations in ns; warmup + timed steps; the forward that gives lse runs once)
+"""
+        with open(PROFILE_BWD_STATS, "w") as f:
+            f.write(bhead + bstats)
+        print(bhead + bstats)
 
 
 def copy_calibration(mib: int) -> None:
