@@ -216,13 +216,34 @@ __device__ __forceinline__ void tr_lane(int lane, int& base, int& x) {
   x = 16 * tswz(row);
 }
 
-template <int NWAVES, int VB16, int NB16, int WI, int HI, bool ATR = false, bool BTR = false>
-__device__ __forceinline__ void nt_mainloop(f32x4 (&acc)[VB16][NB16], uint8_t* lds_w0,
-                                            uint8_t* lds_w1, uint8_t* lds_h0, uint8_t* lds_h1,
-                                            __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rh,
+// One K stage of two K-contiguous operands, staged as rows of kRowBytes: DMA instruction q of
+// this wave fills the 8 staged rows from 8 (q NWAVES + wave); kc is the stage.
+template <int NWAVES, int WI, int HI>
+__device__ __forceinline__ void issue_stage(__amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rh,
                                             const uint32_t (&wgo)[WI], const uint32_t (&hgo)[HI],
-                                            int nk, int wave, int lane, int wv, int wt,
-                                            uint32_t sa = 0, uint32_t sb = 0) {
+                                            int kc, uint8_t* lw, uint8_t* lh, int wave) {
+  const uint32_t so = (uint32_t)kc * kRowBytes;
+#pragma unroll
+  for (int q = 0; q < WI; ++q) dma16(rw, lw + 8 * (q * NWAVES + wave) * kRowBytes, wgo[q], so);
+#pragma unroll
+  for (int q = 0; q < HI; ++q) dma16(rh, lh + 8 * (q * NWAVES + wave) * kRowBytes, hgo[q], so);
+}
+
+struct NoHook {
+  __device__ __forceinline__ void operator()() const {}
+};
+
+// The K loop of one output tile. PRE: the caller has already issued stages 0 and 1 into
+// (lds_w0, lds_h0) and (lds_w1, lds_h1) and every vector memory operation this wave issued
+// since then may be waited for (the loop starts with vmcnt(0)). hook() runs once, after the
+// barrier that publishes stage 0, before any fragment read.
+template <int NWAVES, int VB16, int NB16, int WI, int HI, bool ATR, bool BTR, bool PRE, class Hook>
+__device__ __forceinline__ void nt_mainloop_x(f32x4 (&acc)[VB16][NB16], uint8_t* lds_w0,
+                                              uint8_t* lds_w1, uint8_t* lds_h0, uint8_t* lds_h1,
+                                              __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rh,
+                                              const uint32_t (&wgo)[WI], const uint32_t (&hgo)[HI],
+                                              int nk, int wave, int lane, int wv, int wt,
+                                              uint32_t sa, uint32_t sb, Hook& hook) {
   // sa / sb: bytes from one K stage to the next of a transposed operand (64 rows)
   auto issue = [&](int kc, uint8_t* lw, uint8_t* lh) {
     const uint32_t so = (uint32_t)kc * kRowBytes;
@@ -314,10 +335,15 @@ __device__ __forceinline__ void nt_mainloop(f32x4 (&acc)[VB16][NB16], uint8_t* l
       sub(C1{}, C0{}, nw, nh, 0);
     }
   };
-  issue(0, lds_w0, lds_h0);
-  issue(nk > 1 ? 1 : 0, lds_w1, lds_h1);
-  __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(WI + HI) : "memory");
+  if constexpr (PRE) {
+    wait_dma();
+  } else {
+    issue(0, lds_w0, lds_h0);
+    issue(nk > 1 ? 1 : 0, lds_w1, lds_h1);
+    __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(WI + HI) : "memory");
+  }
   __syncthreads();
+  hook();
   {
     const uint8_t* pa = lds_w0 + a0 + loff[0];
     const uint8_t* pb = lds_h0 + b0 + loff[0];
@@ -345,6 +371,19 @@ __device__ __forceinline__ void nt_mainloop(f32x4 (&acc)[VB16][NB16], uint8_t* l
   // last two stages: nothing left to prefetch (the final fragment reads are unused)
   stage(std::false_type{}, k, lds_w0, lds_h0, lds_w1, lds_h1);
   stage(std::false_type{}, k + 1, lds_w1, lds_h1, lds_w0, lds_h0);
+}
+
+template <int NWAVES, int VB16, int NB16, int WI, int HI, bool ATR = false, bool BTR = false>
+__device__ __forceinline__ void nt_mainloop(f32x4 (&acc)[VB16][NB16], uint8_t* lds_w0,
+                                            uint8_t* lds_w1, uint8_t* lds_h0, uint8_t* lds_h1,
+                                            __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rh,
+                                            const uint32_t (&wgo)[WI], const uint32_t (&hgo)[HI],
+                                            int nk, int wave, int lane, int wv, int wt,
+                                            uint32_t sa = 0, uint32_t sb = 0) {
+  NoHook none;
+  nt_mainloop_x<NWAVES, VB16, NB16, WI, HI, ATR, BTR, false>(acc, lds_w0, lds_w1, lds_h0, lds_h1,
+                                                             rw, rh, wgo, hgo, nk, wave, lane, wv,
+                                                             wt, sa, sb, none);
 }
 
 }  // namespace rlk

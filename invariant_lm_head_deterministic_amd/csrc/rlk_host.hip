@@ -168,7 +168,7 @@ WsMap ws_map(const rlk_logprob_config_t& c, int64_t rows, int32_t n_tiles, int32
     return at;
   };
   const size_t rowsz = (size_t)std::max<int64_t>(rows, 1);
-  m.status = take(4);
+  m.status = take(rlk::kStatusSlotWords * 4);  // status word + LM-head work queues
   m.tgt = take(rowsz * 4);
   m.pm = take((size_t)n_tiles * rowsz * 4);
   m.ps = take((size_t)n_tiles * rowsz * 4);
@@ -246,6 +246,7 @@ rlk_status_t run_rows(const rlk_logprob* h, const Geometry& g, const void* hidde
   a.n_cu = h->n_cu;
   a.portable = (c.flags & RLK_FLAG_PORTABLE_EXP) ? 1 : 0;
   a.inv_tau = c.inv_temperature;
+  a.queue = reinterpret_cast<uint32_t*>(ws + m.status) + rlk::kQueueWord;
   hipError_t e = rlk::launch_lmhead(a, token_tile, ent, st);
   if (e != hipSuccess) return hip_fail(e, "lm-head launch");
   return RLK_OK;
@@ -535,6 +536,8 @@ RLK_API rlk_status_t rlk_logprob_partials(rlk_logprob_t h, const void* hidden,
   const WsMap m = ws_map(c, num_rows, (s1 - s0) * g.tiles_per_seg, 0);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const int g_base = s0 * g.tiles_per_seg;
+  hipError_t e = rlk::launch_clear_status(reinterpret_cast<uint32_t*>(ws + m.status), s);
+  if (e != hipSuccess) return hip_fail(e, "status clear launch");
   st = run_rows(h, g, hidden, W_shard, vocab_begin, targets, rms_gamma, m, ws, num_rows, g_base, 0,
                 num_rows, s0, s1, 0, true, s);
   if (st != RLK_OK) return st;
@@ -554,7 +557,7 @@ RLK_API rlk_status_t rlk_logprob_partials(rlk_logprob_t h, const void* hidden,
   f.n_seg = s1 - s0;
   f.g_base = g_base;
   f.portable = (c.flags & RLK_FLAG_PORTABLE_EXP) ? 1 : 0;
-  hipError_t e = rlk::launch_fold(f, ent, s);
+  e = rlk::launch_fold(f, ent, s);
   if (e != hipSuccess) return hip_fail(e, "segment fold launch");
   return ok();
 }

@@ -39,7 +39,20 @@ struct LmheadArgs {
   int32_t n_cu;             // compute units of the device (picks a launch shape only)
   int32_t portable;         // RLK_FLAG_PORTABLE_EXP: software EXP/LOG (C11p)
   float inv_tau;
+  uint32_t* queue;          // [kQueueWords] work-queue counters of k_lmhead: zero at launch,
+                            // zero again when it ends
+  // k_lmhead's item geometry, set by its launcher (all item counts fit 31 bits)
+  int32_t q_nvb;            // vocab blocks
+  int32_t q_rb;             // row tiles per full band
+  int32_t q_nfull;          // full bands
+  int32_t q_perf;           // items per queue of a full band: ceil(q_nvb q_rb / 8)
+  int32_t q_tail_tt;        // row tiles of the last, partial band (0: none)
+  int32_t q_pert;           // items per queue of that band
 };
+// The workspace's status slot: the status word, then (from word kQueueWord) the queues.
+constexpr int kStatusSlotWords = 32;
+constexpr int kQueueWord = 16;
+constexpr int kQueueWords = 9;
 // A block of the LM-head kernels covers a run of consecutive tiles of one segment (4 tiles,
 // 256 columns, for the MFMA-bound shapes; 3 tiles, 192 columns, for launches of few rows) and
 // a run of rows; each wave of it owns whole tiles, so every tile's reductions stay in one wave.

@@ -82,6 +82,21 @@ __host__ __device__ __forceinline__ int64_t band_blocks(int64_t n_vb, int64_t n_
   return (n_vb * n_tt_band + 7) / 8 * 8;
 }
 
+// The columns and rows of vocab block vb (NTPB tiles of one segment) and row tile tt.
+template <int BT, int NTPB>
+__device__ __forceinline__ void set_tile(const LmheadArgs& a, int vb, int tt, Tile& t) {
+  const int bps = (a.tiles_per_seg + NTPB - 1) / NTPB;
+  const int seg = a.seg_begin + vb / bps;
+  const int jb = vb % bps;
+  const int64_t col0 = (int64_t)jb * NTPB * kVocabTile;
+  // uniform by construction; readfirstlane states that to the compiler
+  t.start = uni64((int64_t)seg * a.seg_len + col0);
+  t.len = uni((int)min((int64_t)NTPB * kVocabTile, a.seg_len - col0));
+  t.tile0 = uni(seg * a.tiles_per_seg + jb * NTPB);
+  t.row0 = uni(tt * BT);
+  t.rows = uni(min(BT, a.rows - tt * BT));
+}
+
 // Block -> (vocab block, row tile), XCD-aware. Row tiles go in bands (band_row_tiles), one band
 // after the other in block order; inside a band, consecutive block ids go round-robin to the 8
 // XCDs, so they are remapped so that each XCD walks a contiguous range of the band's items, a
@@ -113,16 +128,61 @@ __device__ __forceinline__ bool map_tile(const LmheadArgs& a, Tile& t) {
   const int64_t within = L - grp * GV * nb_tt;
   const int vb = first_v + (int)(within % gsz);
   const int tt = tt0 + (int)(within / gsz);
-  const int seg = a.seg_begin + vb / bps;
-  const int jb = vb % bps;
-  const int64_t col0 = (int64_t)jb * NTPB * kVocabTile;
-  // all of it depends on blockIdx only; readfirstlane states that to the compiler
-  t.start = uni64((int64_t)seg * a.seg_len + col0);
-  t.len = uni((int)min((int64_t)NTPB * kVocabTile, a.seg_len - col0));
-  t.tile0 = uni(seg * a.tiles_per_seg + jb * NTPB);
-  t.row0 = uni(tt * BT);
-  t.rows = uni(min(BT, a.rows - tt * BT));
+  set_tile<BT, NTPB>(a, vb, tt, t);
   return true;
+}
+
+// Work queues of the persistent LM-head kernel. A launch's items are its (vocab block, row
+// tile) pairs, band by band; inside a band XCD x owns the contiguous items [x per, (x+1) per),
+// per = ceil(items / 8), in map_tile's order (groups of GV vocab blocks across the band's row
+// tiles, so that one XCD's blocks share W and hidden tiles in its L2). Queue x lists XCD x's
+// items band after band; the c-th is returned in (vb, tt), false past the queue's end.
+constexpr int kQueues = 8;
+__device__ __forceinline__ bool queue_item(const LmheadArgs& a, int x, uint32_t c, int& vb,
+                                           int& tt) {
+  const int nvb = a.q_nvb;
+  const int len_f = max(0, min(a.q_perf, nvb * a.q_rb - x * a.q_perf));  // per full band
+  const uint32_t c_full = (uint32_t)(a.q_nfull * len_f);
+  int band, w, per, nb_tt;
+  if (c < c_full) {
+    band = (int)(c / (uint32_t)len_f);
+    w = (int)c - band * len_f;
+    per = a.q_perf;
+    nb_tt = a.q_rb;
+  } else {
+    band = a.q_nfull;
+    nb_tt = a.q_tail_tt;
+    per = a.q_pert;
+    const int len = max(0, min(per, nvb * nb_tt - x * per));
+    if (c - c_full >= (uint32_t)len) return false;
+    w = (int)(c - c_full);
+  }
+  const int L = x * per + w;
+  constexpr int GV = 8;
+  const int grp = L / (GV * nb_tt);
+  const int first_v = grp * GV;
+  const int gsz = min(GV, nvb - first_v);
+  const int within = L - grp * GV * nb_tt;
+  vb = first_v + within % gsz;
+  tt = band * a.q_rb + within / gsz;
+  return true;
+}
+
+// Hands out one item of queue x (the count of items handed out from it before).
+__device__ __forceinline__ uint32_t claim(uint32_t* q, int x) {
+  return __hip_atomic_fetch_add(q + x, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The item behind claim count c of queue (xq + qi) mod 8; a drained queue moves the block on to
+// the next queue (qi + 1), and false means that all eight are drained. Ends after at most eight
+// claims.
+__device__ __forceinline__ bool next_item(const LmheadArgs& a, int xq, int& qi, uint32_t c,
+                                          int& vb, int& tt) {
+  while (true) {
+    if (queue_item(a, (xq + qi) & (kQueues - 1), c, vb, tt)) return true;
+    if (++qi == kQueues) return false;
+    c = claim(a.queue, (xq + qi) & (kQueues - 1));
+  }
 }
 
 // MFMA layout (v_mfma_f32_16x16x32_bf16, vocab = MFMA rows from W, tokens = MFMA columns from
@@ -253,11 +313,42 @@ __device__ __forceinline__ void tile_epilogue(f32x4 (&acc)[VB16][NB16], const in
   }
 }
 
+// Direct-to-LDS staging of tile t: DMA instruction q of a wave fills the 8 staged rows from
+// 8 (q NWAVES + wave); lane l writes position l & 7 of row (l >> 3) of that group, so it loads
+// the logical piece that the swizzle puts there. Rows past the tile or the launch are clamped to
+// the last valid row (their results are never used), so every address lies inside the tile's
+// descriptor. The per-lane byte offsets are fixed; the K stage is the scalar offset.
+template <int NWAVES, int WI, int HI>
+__device__ __forceinline__ void stage_operands(const LmheadArgs& a, const Tile& t, int wave,
+                                               int lane, uint32_t (&wgo)[WI], uint32_t (&hgo)[HI],
+                                               __amdgpu_buffer_rsrc_t& rw,
+                                               __amdgpu_buffer_rsrc_t& rh) {
+  const int H = a.H;
+#pragma unroll
+  for (int q = 0; q < WI; ++q) {
+    const int r = 8 * (q * NWAVES + wave) + (lane >> 3);
+    const int c = (lane & 7) ^ swz(r);
+    wgo[q] = (uint32_t)(min(r, t.len - 1) * H + c * 8) * 2u;
+  }
+#pragma unroll
+  for (int q = 0; q < HI; ++q) {
+    const int r = 8 * (q * NWAVES + wave) + (lane >> 3);
+    const int c = (lane & 7) ^ swz(r);
+    hgo[q] = (uint32_t)(min(r, t.rows - 1) * H + c * 8) * 2u;
+  }
+  rw = make_rsrc(a.W + (t.start - a.w_row0) * (int64_t)H, t.len * H * 2);
+  rh = make_rsrc(a.hidden + (int64_t)t.row0 * H, t.rows * H * 2);
+}
+
 // --------------------------------------------------------------------------------------------
-// K1: LM-head tile kernel. One block = 4 vocab tiles (256 columns of one segment) x BT rows.
-// Waves: VW split the block's columns, TW split the rows; each wave owns VB16 = 16 / VW vocab
+// K1: LM-head tile kernel. One item = 4 vocab tiles (256 columns of one segment) x BT rows.
+// Waves: VW split the item's columns, TW split the rows; each wave owns VB16 = 16 / VW vocab
 // blocks x NB16 = 2 NTB token blocks of 16 as 16x16 MFMA result tiles (vocab = MFMA rows, tokens
 // = MFMA columns), i.e. whole tiles for its rows, so the epilogue needs no LDS.
+// Persistent: one block per CU takes items from its XCD's queue (queue_item), then from the
+// other XCDs' queues, so a CU that the power limit clocks lower simply takes fewer items, and
+// the first K stages of the next item load while the current one runs its epilogue. Which block
+// computes an item never changes its arithmetic, so the bits do not depend on the schedule.
 // --------------------------------------------------------------------------------------------
 template <int VW, int TW, int NTB, bool ENT, bool TEMP, bool PORT>
 __global__ void __launch_bounds__(64 * VW * TW)
@@ -278,53 +369,104 @@ k_lmhead(const LmheadArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds_h0[BT * kRowBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_h1[BT * kRowBytes];
 
-  Tile t;
-  if (!map_tile<BT, 4>(a, t)) return;
+  // the block's next item (vocab block, row tile), -1 when every queue is drained, and the
+  // queue offset of its claims (from this XCD's queue); written by thread 0, read after barriers
+  __shared__ int s_next[2];
+  __shared__ int s_qi;
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wv = wave % VW;
   const int wt = wave / VW;
-  const int H = a.H;
-  const uint16_t* __restrict__ Wt = a.W + (t.start - a.w_row0) * (int64_t)H;
-  const uint16_t* __restrict__ Ht = a.hidden + (int64_t)t.row0 * H;
+  const int nk = a.H / kKStage;  // even: H is a multiple of 128
+  const bool leader = tid == 0;
+  // this XCD's queue: the XCC_ID hardware register (all 32 bits; the id is bits 3:0)
+  auto xcc_queue = []() { return (int)(__builtin_amdgcn_s_getreg((31 << 11) | 20) & (kQueues - 1)); };
+  // The arguments again from the kernel-argument segment (a is the kernel's only argument, at
+  // offset 0), by scalar loads through a pointer the compiler cannot see through: what the tile
+  // boundary needs is then loaded there instead of held in scalar registers across the K loop,
+  // which has none to spare. (Taking a's address instead would copy it to private memory.)
+  typedef const __attribute__((address_space(4))) LmheadArgs* kargs_t;
+  auto args = []() -> const LmheadArgs& {
+    uint64_t p = (uint64_t)__builtin_amdgcn_kernarg_segment_ptr();
+    __asm__ volatile("" : "+s"(p));
+    return *(const LmheadArgs*)(kargs_t)p;
+  };
+  uint32_t pend = 0;  // thread 0: claim count in flight for the next item
 
-  // Direct-to-LDS staging: DMA instruction q of this wave fills the 8 staged rows starting at
-  // 8 (q * NWAVES + wave); lane l writes position l & 7 of row (l >> 3) of that group, so it
-  // loads the logical piece that the swizzle puts there. Rows past the tile or the launch are
-  // clamped to the last valid row (their results are never used), so every address lies inside
-  // the tile's descriptor. The per-lane byte offsets are fixed; the K stage is the scalar offset.
-  uint32_t wgo[WI], hgo[HI];
-#pragma unroll
-  for (int q = 0; q < WI; ++q) {
-    const int r = 8 * (q * NWAVES + wave) + (lane >> 3);
-    const int c = (lane & 7) ^ swz(r);
-    wgo[q] = (uint32_t)(min(r, t.len - 1) * H + c * 8) * 2u;
+  if (leader) {
+    const int xq = xcc_queue();
+    int qi = 0, vb = -1, tt = 0;
+    if (!next_item(a, xq, qi, claim(a.queue, xq), vb, tt)) vb = -1;
+    s_next[0] = vb;
+    s_next[1] = tt;
+    s_qi = qi;
   }
+  __syncthreads();
+  if (uni(s_next[0]) >= 0) {
+    Tile t;
+    set_tile<BT, 4>(a, uni(s_next[0]), uni(s_next[1]), t);
+    uint32_t wgo[WI], hgo[HI];
+    __amdgpu_buffer_rsrc_t rw, rh;
+    stage_operands<NWAVES, WI, HI>(a, t, wave, lane, wgo, hgo, rw, rh);
+    issue_stage<NWAVES, WI, HI>(rw, rh, wgo, hgo, 0, lds_w0, lds_h0, wave);
+    issue_stage<NWAVES, WI, HI>(rw, rh, wgo, hgo, 1, lds_w1, lds_h1, wave);
+    if (leader) pend = claim(a.queue, (xcc_queue() + s_qi) & (kQueues - 1));
+    // Tile loop. The next item is resolved at the start of this tile's K loop (its claim went
+    // out one tile earlier); once every wave is past this tile's last fragment read, the first
+    // two K stages of the next tile are issued, and only then does this tile's epilogue run.
+    while (true) {
+      f32x4 acc[VB16][NB16];
 #pragma unroll
-  for (int q = 0; q < HI; ++q) {
-    const int r = 8 * (q * NWAVES + wave) + (lane >> 3);
-    const int c = (lane & 7) ^ swz(r);
-    hgo[q] = (uint32_t)(min(r, t.rows - 1) * H + c * 8) * 2u;
+      for (int i = 0; i < VB16; ++i)
+#pragma unroll
+        for (int j = 0; j < NB16; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0f;
+      auto resolve = [&]() {
+        if (leader) {
+          int qi = s_qi, nv = -1, nt = 0;
+          if (!next_item(args(), xcc_queue(), qi, pend, nv, nt)) nv = -1;
+          s_next[0] = nv;
+          s_next[1] = nt;
+          s_qi = qi;
+        }
+      };
+      nt_mainloop_x<NWAVES, VB16, NB16, WI, HI, false, false, true>(
+          acc, lds_w0, lds_w1, lds_h0, lds_h1, rw, rh, wgo, hgo, nk, wave, lane, wv, wt, 0u, 0u,
+          resolve);
+      __syncthreads();
+      const LmheadArgs& b = args();
+      // an opaque copy of the lane id: what the boundary and the epilogue derive from it is
+      // computed here, not hoisted out of the tile loop and held across the K loop
+      int ln = lane;
+      __asm__ volatile("" : "+v"(ln));
+      // the targets of the wave's rows are read only now: held across the K loop they cost
+      // the registers that the loop needs for two waves per SIMD (measured: 4% slower)
+      int ytgt[NB16];
+      load_targets<NB16>(ytgt, b, t, wt, ln);
+      const int nv = uni(s_next[0]);
+      if (nv >= 0) {
+        Tile tn;
+        set_tile<BT, 4>(b, nv, uni(s_next[1]), tn);
+        stage_operands<NWAVES, WI, HI>(b, tn, wave, ln, wgo, hgo, rw, rh);
+        issue_stage<NWAVES, WI, HI>(rw, rh, wgo, hgo, 0, lds_w0, lds_h0, wave);
+        issue_stage<NWAVES, WI, HI>(rw, rh, wgo, hgo, 1, lds_w1, lds_h1, wave);
+        if (leader) pend = claim(b.queue, (xcc_queue() + s_qi) & (kQueues - 1));
+      }
+      tile_epilogue<VB16, NB16, ENT, TEMP, PORT>(acc, ytgt, b, t, wv, wt, ln);
+      if (nv < 0) break;
+      // the next tile again from its item, rather than held across the epilogue
+      __asm__ volatile("" ::: "memory");
+      set_tile<BT, 4>(args(), uni(s_next[0]), uni(s_next[1]), t);
+    }
   }
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(Wt, t.len * H * 2);
-  const __amdgpu_buffer_rsrc_t rh = make_rsrc(Ht, t.rows * H * 2);
-  f32x4 acc[VB16][NB16];
-#pragma unroll
-  for (int i = 0; i < VB16; ++i)
-#pragma unroll
-    for (int j = 0; j < NB16; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0f;
-  // H is a multiple of 128, so the stage count is even
-  nt_mainloop<NWAVES, VB16, NB16, WI, HI>(acc, lds_w0, lds_w1, lds_h0, lds_h1, rw, rh, wgo, hgo,
-                                          H / kKStage, wave, lane, wv, wt);
-
-  // the targets of the wave's rows are read only now: held across the K loop they cost the
-  // registers that the loop needs for two waves per SIMD (measured: 4% slower with spills)
-  int ytgt[NB16];
-  load_targets<NB16>(ytgt, a, t, wt, lane);
-  tile_epilogue<VB16, NB16, ENT, TEMP, PORT>(acc, ytgt, a, t, wv, wt, lane);
+  // the last block of the launch to get here resets the queues for the next launch
+  if (leader && claim(a.queue, kQueues) == gridDim.x - 1) {
+    for (int x = 0; x <= kQueues; ++x)
+      __hip_atomic_exchange(a.queue + x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // --------------------------------------------------------------------------------------------
@@ -698,8 +840,9 @@ __global__ void __launch_bounds__(256) k_rmsnorm(const RmsArgs a) {
   }
 }
 
+// Clears the status word and the LM-head work queues that follow it in its 128-byte slot.
 __global__ void k_clear_status(uint32_t* status) {
-  if (threadIdx.x == 0) *status = 0u;
+  if (threadIdx.x < kStatusSlotWords) status[threadIdx.x] = 0u;
 }
 
 // --------------------------------------------------------------------------------------------
@@ -735,15 +878,28 @@ static void with_modes(const LmheadArgs& a, bool ent, F&& f) {
   }
 }
 
+// Persistent launch: one block per CU (the kernel's LDS allows no second), fewer when there are
+// fewer items; the queues must be zero (k_clear_status), and the kernel leaves them zero.
 template <int VW, int TW, int NTB>
 static hipError_t launch_variant(const LmheadArgs& a, bool ent, hipStream_t s) {
   constexpr int BT = 32 * NTB * TW;
-  const int64_t blocks = lmhead_blocks<BT, 4>(a);
-  if (blocks == 0) return hipSuccess;
-  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const int64_t n_vb = (int64_t)a.n_seg * ((a.tiles_per_seg + 3) / 4);
+  const int64_t n_tt = (a.rows + BT - 1) / BT;
+  const int64_t items = n_vb * n_tt;
+  if (items == 0) return hipSuccess;
+  if (!a.queue || items > 0x7fffffffLL - 8 * 4096) return hipErrorInvalidValue;
+  LmheadArgs q = a;
+  const int64_t rb = band_row_tiles<BT>(a.H);
+  q.q_nvb = (int32_t)n_vb;
+  q.q_rb = (int32_t)std::min(rb, n_tt);
+  q.q_nfull = (int32_t)(n_tt / q.q_rb);
+  q.q_perf = (int32_t)((n_vb * q.q_rb + 7) / 8);
+  q.q_tail_tt = (int32_t)(n_tt - (int64_t)q.q_nfull * q.q_rb);
+  q.q_pert = (int32_t)((n_vb * q.q_tail_tt + 7) / 8);
+  const int64_t blocks = std::min<int64_t>(items, a.n_cu > 0 ? a.n_cu : 256);
   const dim3 grid((unsigned)blocks), block(64 * VW * TW);
   with_modes(a, ent, [&](auto e, auto t, auto p) {
-    hipLaunchKernelGGL((k_lmhead<VW, TW, NTB, e.value, t.value, p.value>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((k_lmhead<VW, TW, NTB, e.value, t.value, p.value>), grid, block, 0, s, q);
   });
   return hipGetLastError();
 }
