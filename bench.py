@@ -239,6 +239,24 @@ bf16_peak_at_sclk_tflops: {PEAK_BF16_TFLOPS * sclk / NOMINAL_SCLK_MHZ:.0f}
         print(bhead + bstats)
 
 
+def diff_stats(got, want) -> dict:
+    """logprob_abs_diff_{mean,max,p50,p90,p99} of two arrays of the same rows."""
+    import numpy as np
+
+    d = np.abs(np.asarray(got, dtype=np.float64) - np.asarray(want, dtype=np.float64))
+    q = np.percentile(d, [50, 90, 99])
+    return {"logprob_abs_diff_mean": float(d.mean()), "logprob_abs_diff_max": float(d.max()),
+            "logprob_abs_diff_p50": float(q[0]), "logprob_abs_diff_p90": float(q[1]),
+            "logprob_abs_diff_p99": float(q[2]), "rows_compared": int(d.size)}
+
+
+def hardware_fingerprint(torch) -> dict:
+    pr = torch.cuda.get_device_properties(0)
+    return {"device": pr.name, "arch": getattr(pr, "gcnArchName", ""),
+            "compute_units": pr.multi_processor_count,
+            "memory_bytes": pr.total_memory, "hip": torch.version.hip, "torch": torch.__version__}
+
+
 def copy_calibration(mib: int) -> None:
     import torch
 
@@ -649,6 +667,20 @@ def main() -> int:
                 tn["_logp"][rows].astype(np.float64) - ref)))
     else:
         result["cpu_baseline"] = None
+    # the report record of the run (requested case, fingerprints, fallbacks, diffs to the oracle)
+    rep = {"requested_case": args.workload, "backend": "rlk_logprob (HIP, gfx950)",
+           "contract_id": lp.contract_id, "build_fingerprint": rlk.rlk_build_fingerprint(),
+           "hardware_fingerprint": hardware_fingerprint(torch),
+           "fallbacks": [],  # the library has no fallback path: an unsupported case is an error
+           "active_token_count": active, "mismatch_count": mismatch,
+           "tokens_per_second": value,
+           "peak_memory_bytes": int(torch.cuda.max_memory_allocated())}
+    if not args.no_cpu_baseline:
+        rep["vs_oracle"] = diff_stats(out_logp[rows], ref)
+        tn = result.get("extras", {}).get("torch_native_lm_head")
+        if tn is not None:
+            rep["torch_native_vs_oracle"] = diff_stats(tn["_logp"][rows], ref)
+    result["report"] = rep
     if "torch_native_lm_head" in result.get("extras", {}):
         result["extras"]["torch_native_lm_head"].pop("_logp")
     print(json.dumps(result), flush=True)
