@@ -196,8 +196,9 @@ class Logprob:
                             _ptr(out.get("entropy")), workspace.data_ptr(),
                             workspace.numel() * workspace.element_size(), s.cuda_stream)
         del keep
-        out["_workspace"] = workspace
-        return out
+        res = dict(out)  # the caller's dict is left as it was given
+        res["_workspace"] = workspace
+        return res
 
     def device_status(self, workspace, stream=None) -> int:
         import torch
