@@ -15,10 +15,13 @@ oracle timed on a bounded sample of the same rows.
     python bench.py --copy-calibration-mib 1024   # a plain device copy, for PMC byte scaling
     python bench.py --pmc-summary DIR             # profiles/ summaries from rocprofv3 output
     python bench.py --backward-only --steps 5     # the backward alone (for its kernel summary)
+    python bench.py --rollout-only --steps 3      # the rollout layout alone (decode batches x 4 shards)
 
 The PMC summary (profiles/lmhead_qwen3_8b_head_pmc.txt) is written from five rocprofv3 runs of
 this script, each into its own folder under DIR (the commands are printed into the summary), and
-the backward's kernel summary from a sixth (bwd: --kernel-trace --stats, --backward-only):
+the backward's kernel summary from a sixth (bwd: --kernel-trace --stats, --backward-only), and
+the rollout layout's summary from two more (rollout: --kernel-trace --stats, --rollout-only;
+rfetch: --pmc FETCH_SIZE --kernel-trace, --rollout-only):
   stats   --kernel-trace --stats, default step counts     (kernel durations)
   fetch   --pmc FETCH_SIZE GRBM_GUI_ACTIVE --kernel-trace (bytes read from HBM/MALL, clock)
   write   --pmc WRITE_SIZE SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE --kernel-trace
@@ -52,6 +55,9 @@ NOMINAL_SCLK_MHZ = 2400.0  # the clock the published MFMA peak is quoted at
 PROF_ARGS = "--steps 3 --warmup 1 --no-cpu-baseline --no-layout-check --no-extras"
 STATS_ARGS = "--steps 30 --warmup 3 --no-cpu-baseline --no-layout-check --no-extras"
 BWD_ARGS = "--backward-only --steps 5 --warmup 2"
+ROLLOUT_ARGS = "--rollout-only --steps 3 --warmup 1"
+ROLLOUT_PMC_ARGS = "--rollout-only --steps 1 --warmup 1"
+PROFILE_ROLLOUT = os.path.join(ROOT, "profiles", "lmhead_decode_rollout_kernel_stats.txt")
 # the sources the LM-head kernel is compiled from (its file, the shared K loop and primitives,
 # the argument structs): a change to any of them makes the committed PMC figures stale
 KERNEL_SRCS = [os.path.join(ROOT, "invariant_lm_head_deterministic_amd", "csrc", f)
@@ -165,6 +171,8 @@ def write_pmc_summary(base: str) -> None:
         "cfetch": ("--pmc FETCH_SIZE", "--copy-calibration-mib 1024"),
         "cwrite": ("--pmc WRITE_SIZE", "--copy-calibration-mib 1024"),
         "bwd": ("--kernel-trace --stats", BWD_ARGS),
+        "rollout": ("--kernel-trace --stats", ROLLOUT_ARGS),
+        "rfetch": ("--pmc FETCH_SIZE --kernel-trace", ROLLOUT_PMC_ARGS),
     }
     cmds = {k: cmd.format(opts=o, d=os.path.join(base, k), args=a) for k, (o, a) in runs.items()}
     mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
@@ -237,6 +245,41 @@ bf16_peak_at_sclk_tflops: {PEAK_BF16_TFLOPS * sclk / NOMINAL_SCLK_MHZ:.0f}
         with open(PROFILE_BWD_STATS, "w") as f:
             f.write(bhead + bstats)
         print(bhead + bstats)
+    if os.path.isdir(os.path.join(base, "rollout")) and os.path.isdir(os.path.join(base, "rfetch")):
+        write_rollout_summary(base, cmds, f_scale)
+
+
+def write_rollout_summary(base: str, cmds: dict, f_scale: float) -> None:
+    """profiles/ summary of the rollout layout: per-launch durations of the decode LM-head kernels
+    (kernel trace) and their bytes fetched past the L2 (FETCH_SIZE, copy-scaled)."""
+    mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
+    rd = os.path.join(base, "rollout")
+    stats = open(_one(rd, "kernel_stats.csv")).read()
+    dur = _durations(rd, "k_lmhead")
+    cf = _counters(os.path.join(base, "rfetch"), "k_lmhead")
+    w_shard = (151936 // 4) * 4096 * 2
+    per_step_launches = 120
+    n = len(dur)
+    tot_ms = sum(dur.values()) / 1e6
+    fetch = [v * 1024 / f_scale for _, v in cf["FETCH_SIZE"]]
+    text = f"""# Decode LM-head kernels, rollout layout of the qwen3_8b_head workload: 4096 rows as 30 decode
+# batches of 1..256 rows, each over 4 vocab shards of 37984 rows (120 launches per step, every
+# launch streams its 311 MB shard of W from HBM)
+# commands (from the repository root, TMPDIR=/tmp):
+#   {cmds["rollout"]}
+#   {cmds["rfetch"]}
+#   (FETCH_SIZE scaled by the 1 GiB copy of: {cmds["cfetch"]})
+# kernel_source_sha256: {kernel_source_sha()}
+lmhead_launches: {n} ({n // per_step_launches} steps incl. warmup)
+lmhead_mean_us_per_launch: {tot_ms * 1e3 / n:.1f}
+w_stream_GBps_from_trace: {n * w_shard / (tot_ms * 1e-3) / 1e9:.0f}
+w_stream_frac_of_8TBps: {n * w_shard / (tot_ms * 1e-3) / 8e12:.3f}
+fetch_bytes_per_launch_mean: {mean(fetch):.4g}
+fetch_over_w_shard_bytes: {mean(fetch) / w_shard:.3f}
+"""
+    with open(PROFILE_ROLLOUT, "w") as f:
+        f.write(text + "# run_kernel_stats.csv (durations in ns)\n" + stats)
+    print(text + stats)
 
 
 def diff_stats(got, want) -> dict:
@@ -450,25 +493,34 @@ def backward(rlk, np, torch, hd, Wd, yd, w, steps: int = 5, warmup: int = 2) -> 
                 rlk.make_config(w.H, w.V, w.segments), w.T, 0)}
 
 
+def rollout(rlk, datagen, np, hd, Wd, yd, w, ref_logp, steps: int = 3, warmup: int = 1) -> dict:
+    """The rollout layout of the TP4 workload: the rows as decode batches of 1..256, each over the
+    4 vocab shards (one LM-head launch per batch and shard, W streamed from HBM every time)."""
+    lp = rlk.Logprob(w.H, w.V, vocab_segments=w.segments, device=0)
+    sizes = datagen.decode_layout(w.T)
+    r = time_layout(rlk, lp, hd, Wd, yd, None, w.T, steps, warmup,
+                    dict(batch_sizes=sizes, vocab_shards=4))
+    w_bytes = r["lmhead_launches_per_step"] * (w.V // 4) * w.H * 2
+    res = {
+        "decode_batches": len(sizes), "lmhead_launches_per_step": r["lmhead_launches_per_step"],
+        "ms_per_step": r["ms_per_step"], "tokens_per_s": w.T / (r["ms_per_step"] * 1e-3),
+        "lmhead_ms_per_step": r["lmhead_ms_per_step"],
+        "w_stream_GBps": w_bytes / (r["lmhead_ms_per_step"] * 1e-3) / 1e9,
+        "hbm_frac": w_bytes / (r["lmhead_ms_per_step"] * 1e-3) / 8e12}
+    if ref_logp is not None:
+        res["mismatch_count_vs_one_pass"] = int(np.count_nonzero(
+            r["_logp"].view(np.uint32) != ref_logp.view(np.uint32)))
+    return res
+
+
 def extras(rlk, datagen, np, torch, hd, Wd, yd, w, ref_logp) -> dict:
     """The other rows of the path, measured next to the headline: the rollout layout of the TP4
     workload (decode batches x 4 vocab shards; HBM-bound W stream), the same batch with the
     portable software EXP/LOG, a plain framework LM head on the same rows, the long GRPO batch in
     one pass and in chunks, and the fused final RMSNorm + temperature + entropy head."""
     out = {}
-    lp = rlk.Logprob(w.H, w.V, vocab_segments=w.segments, device=0)
+    out["tp4_decode_x4_shards"] = rollout(rlk, datagen, np, hd, Wd, yd, w, ref_logp)
     sizes = datagen.decode_layout(w.T)
-    r = time_layout(rlk, lp, hd, Wd, yd, None, w.T, 3, 1,
-                    dict(batch_sizes=sizes, vocab_shards=4))
-    w_bytes = r["lmhead_launches_per_step"] * (w.V // 4) * w.H * 2
-    out["tp4_decode_x4_shards"] = {
-        "decode_batches": len(sizes), "lmhead_launches_per_step": r["lmhead_launches_per_step"],
-        "ms_per_step": r["ms_per_step"], "tokens_per_s": w.T / (r["ms_per_step"] * 1e-3),
-        "w_stream_GBps": w_bytes / (r["lmhead_ms_per_step"] * 1e-3) / 1e9,
-        "hbm_frac": w_bytes / (r["lmhead_ms_per_step"] * 1e-3) / 8e12,
-        "mismatch_count_vs_one_pass": int(np.count_nonzero(
-            r["_logp"].view(np.uint32) != ref_logp.view(np.uint32)))}
-    del lp
     log("extras: portable primitives")
     lpp = rlk.Logprob(w.H, w.V, vocab_segments=w.segments, device=0, portable=True)
     r = time_layout(rlk, lpp, hd, Wd, yd, None, w.T, 5, 2, {})
@@ -526,6 +578,8 @@ def main() -> int:
                     help="skip the rollout-layout and norm_head measurements")
     ap.add_argument("--backward-only", action="store_true",
                     help="time only the backward of the workload (for its rocprofv3 summary)")
+    ap.add_argument("--rollout-only", action="store_true",
+                    help="time only the rollout layout (decode batches x 4 vocab shards)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -561,6 +615,10 @@ def main() -> int:
     Wd = torch.from_numpy(Wb.view(np.int16)).to(dev)
     yd = torch.from_numpy(y.astype(np.int32)).to(dev)
     gd = None if gamma is None else torch.from_numpy(gamma.view(np.int16)).to(dev)
+    if args.rollout_only:
+        r = rollout(rlk, datagen, np, hd, Wd, yd, w, None, steps=args.steps, warmup=args.warmup)
+        print(json.dumps({"what": "rollout layout", "workload": args.workload, **r}), flush=True)
+        return 0
     if args.backward_only:
         r = backward(rlk, np, torch, hd, Wd, yd, w, steps=args.steps, warmup=args.warmup)
         print(json.dumps({"what": "backward", "workload": args.workload, **r}), flush=True)
