@@ -476,10 +476,11 @@ k_lmhead(const LmheadArgs a) {
 // batch has one row tile, so a launch has few blocks and the W stream is bound by the bytes
 // each block keeps in flight: these variants cycle NS (2-4) LDS stages, so NS-1 stages of DMA
 // are outstanding while one is read.
-// SPLIT: W streams through its own ring of NS stages and the hidden rows through a ring of 2
-// (they are L2-resident and arrive quickly), so the same LDS holds one more W stage in flight;
-// measured faster for the largest decode batches (193-256 rows: 106 -> 92 us per vocab segment)
-// and slower for smaller ones, whose short stages leave the hidden rows too little time.
+// HS > 0: W streams through its own ring of NS stages and the hidden rows through a ring of HS
+// (they are L2-resident and arrive quickly), so the same LDS holds more W in flight. Measured
+// per vocab segment: 193-256 rows 106 -> 92 us (3 + 2 stages), 65-128 rows 74 -> 73 us
+// (4 + 3); no gain for 129-192 rows, and slower at <= 64 rows with a ring of 2 for the hidden
+// rows, whose short stages leave those too little time.
 // The stage buffer is picked at run time; the DMA is issued from inline assembly so that the
 // compiler, which cannot tell the stage buffers apart at run time, does not wait for every
 // outstanding DMA before each LDS read. Its completion is awaited explicitly (vmcnt) before the
@@ -514,7 +515,7 @@ __device__ __forceinline__ void wait_vm() {
   __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(D) : "memory");
 }
 
-template <int VW, int TW, int NTB, int NS, int NTPB, bool SPLIT, bool ENT, bool TEMP, bool PORT>
+template <int VW, int TW, int NTB, int NS, int NTPB, int HS, bool ENT, bool TEMP, bool PORT>
 __global__ void __launch_bounds__(64 * VW * TW) k_lmhead_deep(const LmheadArgs a) {
   constexpr int NWAVES = VW * TW;
   constexpr int BT = 32 * NTB * TW;
@@ -530,8 +531,11 @@ __global__ void __launch_bounds__(64 * VW * TW) k_lmhead_deep(const LmheadArgs a
   constexpr int SH = 8 * HI * NWAVES * kRowBytes;
   static_assert(VB16 * VW * 16 == BW && VB16 % 4 == 0 && WI * 8 * NWAVES == BW && BT % 32 == 0,
                 "tiling");
-  static_assert(NS >= 2 && NS <= 4 && (NS - 2) * DPS <= 63 && (NS - 1) * WI <= 63, "stages");
-  constexpr int NSH = SPLIT ? 2 : NS;  // stages of the hidden rows' ring
+  static_assert(NS >= 2 && NS <= 6 && (NS - 2) * DPS <= 63 && (NS - 1) * (HI + WI) <= 63,
+                "stages");
+  constexpr bool SPLIT = HS > 0;      // separate rings for W and the hidden rows
+  constexpr int NSH = SPLIT ? HS : NS;  // stages of the hidden rows' ring
+  static_assert(!SPLIT || (HS >= 2 && HS < NS), "rings");
 
   __shared__ __attribute__((aligned(1024))) uint8_t lds_w[NS * SW];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_h[NSH * SH];
@@ -630,24 +634,25 @@ __global__ void __launch_bounds__(64 * VW * TW) k_lmhead_deep(const LmheadArgs a
   };
 
   if constexpr (SPLIT) {
-    // Issue order: H0 W0 H1 W1 .. W(NS-1), then after each barrier H(k+2) and W(k+NS). Loads
-    // complete in issue order, so waiting for H(k+1) leaves only W(k+NS-1) in flight: W stage
-    // k+NS has NS-1 stages of time to land, the hidden rows' stage k+2 one.
-    issue_h(0);
-    issue_w(0);
-    if (nk > 1) issue_h(1);
-    for (int j = 1; j < NS && j < nk; ++j) issue_w(j);
-    if (nk >= NS) wait_vm<(NS - 1) * WI>();
+    // Issue order: stage by stage, H(j) (j < HS) then W(j) (j < NS); after the barrier of stage
+    // k, H(k+HS) and W(k+NS). Loads complete in issue order, so waiting for H(k+1) leaves in
+    // flight only what was issued after it: W(k+1-HS+NS) and the HS-2 later stages' pairs.
+    // W stage k+NS then has NS-1 stages of time to land, the hidden rows' stage k+HS HS-1.
+    for (int j = 0; j < NS && j < nk; ++j) {
+      if (j < HS) issue_h(j);
+      issue_w(j);
+    }
+    if (nk >= NS) wait_vm<(HS - 1) * HI + (NS - 1) * WI>();  // H0 and W0 have landed
     else wait_vm<0>();
     __syncthreads();
     load_frags(0, 0, 0);
     for (int k = 0; k < nk; ++k) {
       mfmas(0);
       load_frags(k, 1, 1);
-      if (k - 1 + NS < nk) wait_vm<WI>();
+      if (k - 1 + NS < nk) wait_vm<WI + (HS - 2) * (HI + WI)>();
       else wait_vm<0>();
       __syncthreads();
-      if (k + 2 < nk) issue_h(k + 2);  // into stage k's buffers, free after the barrier
+      if (k + HS < nk) issue_h(k + HS);  // into stage k's buffers, free after the barrier
       if (k + NS < nk) issue_w(k + NS);
       mfmas(1);
       load_frags(k + 1, 0, 0);
@@ -941,7 +946,7 @@ static hipError_t launch_variant(const LmheadArgs& a, bool ent, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int VW, int TW, int NTB, int NS, int NTPB, bool SPLIT = false>
+template <int VW, int TW, int NTB, int NS, int NTPB, int HS = 0>
 static hipError_t launch_deep(const LmheadArgs& a, bool ent, hipStream_t s) {
   constexpr int BT = 32 * NTB * TW;
   const int64_t blocks = lmhead_blocks<BT, NTPB>(a);
@@ -949,7 +954,7 @@ static hipError_t launch_deep(const LmheadArgs& a, bool ent, hipStream_t s) {
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)blocks), block(64 * VW * TW);
   with_modes(a, ent, [&](auto e, auto t, auto p) {
-    hipLaunchKernelGGL((k_lmhead_deep<VW, TW, NTB, NS, NTPB, SPLIT, e.value, t.value, p.value>), grid,
+    hipLaunchKernelGGL((k_lmhead_deep<VW, TW, NTB, NS, NTPB, HS, e.value, t.value, p.value>), grid,
                        block, 0, s, a);
   });
   return hipGetLastError();
@@ -973,9 +978,9 @@ hipError_t launch_lmhead(const LmheadArgs& a, int bt, bool ent, hipStream_t s) {
   if (bt == 0) {
     if (a.rows > 256) return launch_variant<2, 4, 2>(a, ent, s);
     if (three_tile_blocks(a)) {
-      if (a.rows > 192) return launch_deep<3, 4, 2, 3, 3, true>(a, ent, s);
+      if (a.rows > 192) return launch_deep<3, 4, 2, 3, 3, 2>(a, ent, s);
       if (a.rows > 128) return launch_deep<3, 2, 3, 3, 3>(a, ent, s);
-      if (a.rows > 64) return launch_deep<3, 2, 2, 3, 3>(a, ent, s);
+      if (a.rows > 64) return launch_deep<3, 2, 2, 4, 3, 3>(a, ent, s);
       return launch_deep<3, 2, 1, 3, 3>(a, ent, s);
     }
     bt = a.rows > 128 ? 256 : a.rows > 64 ? 128 : a.rows > 32 ? 64 : 32;
