@@ -61,7 +61,7 @@ PROFILE_ROLLOUT = os.path.join(ROOT, "profiles", "lmhead_decode_rollout_kernel_s
 # the sources the LM-head kernel is compiled from (its file, the shared K loop and primitives,
 # the argument structs): a change to any of them makes the committed PMC figures stale
 KERNEL_SRCS = [os.path.join(ROOT, "invariant_lm_head_deterministic_amd", "csrc", f)
-               for f in ("rlk_kernels.hip", "rlk_device.h", "rlk_internal.h")]
+               for f in ("rlk_kernels.hip", "rlk_device.h", "rlk_internal.h", "rlk_queue.h")]
 
 
 def log(msg: str) -> None:

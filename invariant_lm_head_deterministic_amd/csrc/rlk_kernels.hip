@@ -54,6 +54,7 @@
 //     epsilon, output boundary; wave64 shuffle steps in a fixed order, nxbn.cn blog §3.2).
 
 #include "rlk_device.h"
+#include "rlk_queue.h"
 
 namespace rlk {
 
@@ -129,42 +130,6 @@ __device__ __forceinline__ bool map_tile(const LmheadArgs& a, Tile& t) {
   const int vb = first_v + (int)(within % gsz);
   const int tt = tt0 + (int)(within / gsz);
   set_tile<BT, NTPB>(a, vb, tt, t);
-  return true;
-}
-
-// Work queues of the persistent LM-head kernel. A launch's items are its (vocab block, row
-// tile) pairs, band by band; inside a band XCD x owns the contiguous items [x per, (x+1) per),
-// per = ceil(items / 8), in map_tile's order (groups of GV vocab blocks across the band's row
-// tiles, so that one XCD's blocks share W and hidden tiles in its L2). Queue x lists XCD x's
-// items band after band; the c-th is returned in (vb, tt), false past the queue's end.
-constexpr int kQueues = 8;
-__device__ __forceinline__ bool queue_item(const LmheadArgs& a, int x, uint32_t c, int& vb,
-                                           int& tt) {
-  const int nvb = a.q_nvb;
-  const int len_f = max(0, min(a.q_perf, nvb * a.q_rb - x * a.q_perf));  // per full band
-  const uint32_t c_full = (uint32_t)(a.q_nfull * len_f);
-  int band, w, per, nb_tt;
-  if (c < c_full) {
-    band = (int)(c / (uint32_t)len_f);
-    w = (int)c - band * len_f;
-    per = a.q_perf;
-    nb_tt = a.q_rb;
-  } else {
-    band = a.q_nfull;
-    nb_tt = a.q_tail_tt;
-    per = a.q_pert;
-    const int len = max(0, min(per, nvb * nb_tt - x * per));
-    if (c - c_full >= (uint32_t)len) return false;
-    w = (int)(c - c_full);
-  }
-  const int L = x * per + w;
-  constexpr int GV = 8;
-  const int grp = L / (GV * nb_tt);
-  const int first_v = grp * GV;
-  const int gsz = min(GV, nvb - first_v);
-  const int within = L - grp * GV * nb_tt;
-  vb = first_v + within % gsz;
-  tt = band * a.q_rb + within / gsz;
   return true;
 }
 
@@ -931,13 +896,7 @@ static hipError_t launch_variant(const LmheadArgs& a, bool ent, hipStream_t s) {
   if (items == 0) return hipSuccess;
   if (!a.queue || items > 0x7fffffffLL - 8 * 4096) return hipErrorInvalidValue;
   LmheadArgs q = a;
-  const int64_t rb = band_row_tiles<BT>(a.H);
-  q.q_nvb = (int32_t)n_vb;
-  q.q_rb = (int32_t)std::min(rb, n_tt);
-  q.q_nfull = (int32_t)(n_tt / q.q_rb);
-  q.q_perf = (int32_t)((n_vb * q.q_rb + 7) / 8);
-  q.q_tail_tt = (int32_t)(n_tt - (int64_t)q.q_nfull * q.q_rb);
-  q.q_pert = (int32_t)((n_vb * q.q_tail_tt + 7) / 8);
+  queue_setup(q, n_vb, n_tt, band_row_tiles<BT>(a.H));
   const int64_t blocks = std::min<int64_t>(items, a.n_cu > 0 ? a.n_cu : 256);
   const dim3 grid((unsigned)blocks), block(64 * VW * TW);
   with_modes(a, ent, [&](auto e, auto t, auto p) {
