@@ -3,9 +3,10 @@ row, workspace and output offset needs 64-bit arithmetic. The one-pass result is
 row chunks bit for bit, and sampled rows (the first, the last, and rows around 2^20 and 2^21)
 with the float64 oracle.
 
-The long GRPO batch on the pages is 55296 rows (8 samples x 6912 tokens, Qwen3-8B GRPO run on
-the vime page); a rollout service batches far more rows than that, and the contract must not
-change with the row count (RL-Kernel v0.1.0 summary, "Numeric execution contract").
+The GRPO run the pages report samples 8 responses per prompt of up to 6912 tokens (aihirek.info
+report on the Qwen3-8B run); a rollout service batches far more rows than one such batch, and
+the contract must not change with the row count (RL-Kernel v0.1.0 summary, "Numeric execution
+contract").
 """
 
 import numpy as np
