@@ -417,6 +417,17 @@ def torch_native(np, torch, hd, Wd, yd, sizes, ref_logp, steps: int = 5, warmup:
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
+    # the vendor GEMM alone (bf16 logits, no log-softmax): the same contraction without the
+    # fused epilogue, on the same box and the same operands
+    for _ in range(warmup):
+        torch.nn.functional.linear(h, W)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        torch.nn.functional.linear(h, W)
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_ms = e0.elapsed_time(e1) / steps
     one_h = one.cpu().numpy()
     offs = np.concatenate([[0], np.cumsum(sizes)])
     parts = [run(slice(int(offs[i]), int(offs[i + 1]))) for i in range(len(sizes))]
@@ -425,6 +436,9 @@ def torch_native(np, torch, hd, Wd, yd, sizes, ref_logp, steps: int = 5, warmup:
     T = int(h.shape[0])
     return {"what": "F.linear (bf16 logits) + fp32 log_softmax + gather",
             "ms_per_step": ms, "tokens_per_s": int(active.sum().item()) / (ms * 1e-3),
+            "vendor_gemm_only_ms": gemm_ms,
+            "vendor_gemm_only_frac_of_bf16_peak":
+                2.0 * h.shape[0] * h.shape[1] * W.shape[0] / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
             "mismatch_count_decode_batches_vs_one_pass": int(np.count_nonzero(
                 dec.view(np.uint32) != one_h.view(np.uint32))),
             "rows": T, "max_abs_diff_vs_this_library": float(np.max(np.abs(
