@@ -8,6 +8,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "rlk_internal.h"
 

@@ -154,7 +154,7 @@ rlk_status_t plan_layout(const rlk_logprob_config_t& c, const rlk_layout_desc_t*
 
 // Workspace map (offsets in bytes, each 256-aligned).
 struct WsMap {
-  size_t status, tgt, pm, ps, pu, rec, y, total;
+  size_t status, tgt, pm, ps, pu, rec, y, done, total;
 };
 
 WsMap ws_map(const rlk_logprob_config_t& c, int64_t rows, int32_t n_tiles, int32_t n_rec_seg) {
@@ -175,6 +175,7 @@ WsMap ws_map(const rlk_logprob_config_t& c, int64_t rows, int32_t n_tiles, int32
   m.pu = ent ? take((size_t)n_tiles * rowsz * 4) : 0;
   m.rec = n_rec_seg ? take((size_t)n_rec_seg * rowsz * sizeof(rlk_segment_record_t)) : 0;
   m.y = rms ? take(rowsz * (size_t)c.hidden_size * 2) : 0;
+  m.done = n_rec_seg ? take((rowsz + 63) / 64 * 4) : 0;  // fused-merge counters per 64 rows
   m.total = off;
   return m;
 }
@@ -391,7 +392,8 @@ rlk_status_t forward_impl(rlk_logprob_t h, const void* hidden, const void* W_lm,
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint32_t* status = reinterpret_cast<uint32_t*>(ws + m.status);
-  hipError_t e = rlk::launch_clear_status(status, s);
+  uint32_t* done = reinterpret_cast<uint32_t*>(ws + m.done);
+  hipError_t e = rlk::launch_clear_status(status, done, (T + 63) / 64, s);
   if (e != hipSuccess) return hip_fail(e, "status clear launch");
   if (T == 0) return ok();
 
@@ -438,9 +440,9 @@ rlk_status_t forward_impl(rlk_logprob_t h, const void* hidden, const void* W_lm,
     f.n_seg = c.vocab_segments;
     f.g_base = 0;
     f.portable = (c.flags & RLK_FLAG_PORTABLE_EXP) ? 1 : 0;
-    e = rlk::launch_fold(f, ent, s);
-    if (e != hipSuccess) return hip_fail(e, "segment fold launch");
-    rlk::MergeArgs mg;
+    // the fold of each row block's last segment also merges the segments (C9, C10)
+    f.done = done;
+    rlk::MergeArgs& mg = f.mg;
     mg.rec = reinterpret_cast<const rlk_segment_record_t*>(ws + m.rec) + br.begin;
     mg.targets = targets + br.begin;
     mg.logp = logp + br.begin;
@@ -452,9 +454,9 @@ rlk_status_t forward_impl(rlk_logprob_t h, const void* hidden, const void* W_lm,
     mg.vocab = c.vocab_size;
     mg.rows = (int32_t)n;
     mg.n_seg = c.vocab_segments;
-    mg.portable = (c.flags & RLK_FLAG_PORTABLE_EXP) ? 1 : 0;
-    e = rlk::launch_merge(mg, ent, s);
-    if (e != hipSuccess) return hip_fail(e, "merge launch");
+    mg.portable = f.portable;
+    e = rlk::launch_fold(f, ent, s);
+    if (e != hipSuccess) return hip_fail(e, "segment fold launch");
   }
   return ok();
 }
@@ -536,7 +538,7 @@ RLK_API rlk_status_t rlk_logprob_partials(rlk_logprob_t h, const void* hidden,
   const WsMap m = ws_map(c, num_rows, (s1 - s0) * g.tiles_per_seg, 0);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const int g_base = s0 * g.tiles_per_seg;
-  hipError_t e = rlk::launch_clear_status(reinterpret_cast<uint32_t*>(ws + m.status), s);
+  hipError_t e = rlk::launch_clear_status(reinterpret_cast<uint32_t*>(ws + m.status), nullptr, 0, s);
   if (e != hipSuccess) return hip_fail(e, "status clear launch");
   st = run_rows(h, g, hidden, W_shard, vocab_begin, targets, rms_gamma, m, ws, num_rows, g_base, 0,
                 num_rows, s0, s1, 0, true, s);
@@ -557,6 +559,8 @@ RLK_API rlk_status_t rlk_logprob_partials(rlk_logprob_t h, const void* hidden,
   f.n_seg = s1 - s0;
   f.g_base = g_base;
   f.portable = (c.flags & RLK_FLAG_PORTABLE_EXP) ? 1 : 0;
+  f.done = nullptr;  // records only: the merge runs after the shards are gathered
+  f.mg = rlk::MergeArgs{};
   e = rlk::launch_fold(f, ent, s);
   if (e != hipSuccess) return hip_fail(e, "segment fold launch");
   return ok();

@@ -57,6 +57,21 @@ constexpr int kQueueWords = 9;
 // 256 columns, for the MFMA-bound shapes; 3 tiles, 192 columns, for launches of few rows) and
 // a run of rows; each wave of it owns whole tiles, so every tile's reductions stay in one wave.
 
+struct MergeArgs {
+  const rlk_segment_record_t* rec;  // [n_seg][rec_ld], all segments of the vocabulary
+  const int32_t* targets;
+  float* logp;
+  float* lse;
+  float* entropy;           // null without entropy
+  uint32_t* status;         // null allowed
+  int64_t rec_ld;
+  int64_t seg_len;
+  int64_t vocab;
+  int32_t rows;
+  int32_t n_seg;
+  int32_t portable;
+};
+
 struct FoldArgs {
   const float* part_m;
   const float* part_s;
@@ -73,21 +88,11 @@ struct FoldArgs {
   int32_t n_seg;
   int32_t g_base;
   int32_t portable;
-};
-
-struct MergeArgs {
-  const rlk_segment_record_t* rec;  // [n_seg][rec_ld], all segments of the vocabulary
-  const int32_t* targets;
-  float* logp;
-  float* lse;
-  float* entropy;           // null without entropy
-  uint32_t* status;         // null allowed
-  int64_t rec_ld;
-  int64_t seg_len;
-  int64_t vocab;
-  int32_t rows;
-  int32_t n_seg;
-  int32_t portable;
+  // Fused merge: null, or one counter per 64-row block of the launch (zero on entry, zero again
+  // on exit); the fold of a row block's last segment then also writes mg's outputs for it. Needs
+  // the launch to cover every segment of the vocabulary (mg.rec = rec).
+  uint32_t* done;
+  MergeArgs mg;
 };
 
 struct RmsArgs {
@@ -180,6 +185,7 @@ hipError_t launch_lmhead(const LmheadArgs& a, int token_tile, bool entropy, hipS
 hipError_t launch_fold(const FoldArgs& a, bool entropy, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, bool entropy, hipStream_t s);
 hipError_t launch_rmsnorm(const RmsArgs& a, hipStream_t s);
-hipError_t launch_clear_status(uint32_t* status, hipStream_t s);
+// Zeroes the status slot (status word and LM-head work queues) and n_done fused-merge counters.
+hipError_t launch_clear_status(uint32_t* status, uint32_t* done, int64_t n_done, hipStream_t s);
 
 }  // namespace rlk

@@ -648,17 +648,237 @@ __global__ void __launch_bounds__(64 * VW * TW) k_lmhead_deep(const LmheadArgs a
 }
 
 // --------------------------------------------------------------------------------------------
+// K1s: streaming LM-head kernel for launches of at most 256 rows (decode batches). Same MFMA
+// chain (C1), fragment order and per-tile epilogue as k_lmhead, hence the same bits.
+//
+// A decode launch is bound by the W stream: every W row is used by at most 256 rows. Loads
+// complete in issue order per wave, so a wave that waits for a recent load also waits for every
+// older one; kernels whose waves both stream W and read the hidden rows keep W only as deep in
+// flight as the hidden rows. Here the two streams come from different waves:
+//  - NPW producer waves only copy W into a ring of NS LDS stages (64 W rows x 64 K each), keeping
+//    NS-1 stages in flight and waiting, before each stage's barrier, only for their own copy of
+//    that stage;
+//  - 4 compute waves read the stage's W fragments from LDS and their own hidden rows straight
+//    from memory into registers (the rows of a decode batch stay in L2), HD stages ahead.
+// One block per CU; an item is one 64-column tile with all the launch's rows (wave w owns token
+// blocks NBW w .. NBW w + NBW - 1), so a CU streams whole tiles one after the other without
+// draining its ring between them, and every CU of the device takes part. Block b takes the
+// items b, b + G, b + 2G, ... of the launch (G blocks).
+// --------------------------------------------------------------------------------------------
+
+// f(integral_constant<int, S>) for each S of the sequence, in order.
+template <class F, int... S>
+__device__ __forceinline__ void unroll_seq(std::integer_sequence<int, S...>, F&& f) {
+  (f(std::integral_constant<int, S>{}), ...);
+}
+
+// s_waitcnt vmcnt(n * D) for a run-time n in [0, N] (one branch per value).
+template <int D, int N>
+__device__ __forceinline__ void wait_vm_n(int n) {
+  if constexpr (N == 0) {
+    wait_vm<0>();
+  } else {
+    if (n >= N) wait_vm<N * D>();
+    else wait_vm_n<D, N - 1>(n);
+  }
+}
+
+template <int CW, int NBW, int SK, int NS, int NPW, int HD, bool ENT, bool TEMP, bool PORT>
+__global__ void __launch_bounds__(64 * (CW + NPW)) k_lmhead_stream(const LmheadArgs a) {
+  constexpr int RB = 2 * SK;                // bytes of one staged W row
+  constexpr int SW = kVocabTile * RB;       // bytes of one W stage (64 rows x SK of K)
+  constexpr int DPS = SW / 1024;            // DMA instructions per stage (1 KB each)
+  constexpr int DPW = DPS / NPW;            // ... per producer wave
+  constexpr int KS = SK / 32;               // MFMA K-steps per stage
+  constexpr int RPI = 1024 / RB;            // staged rows per DMA instruction
+  static_assert((SK == 128 || SK == 256) && NPW * DPW == DPS && NS >= 3 && (NS - 2) * DPW <= 63,
+                "stages");
+  static_assert(HD >= 1, "hidden prefetch");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_w[NS * SW];
+  // Staged rows of RB = 256 or 512 bytes: piece c (16 bytes) of row r sits at position
+  // c ^ (r & 15), so a fragment read (16 consecutive rows, one piece each) covers the 64 banks
+  // once.
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int H = a.H;
+  const int nk = H / SK;  // the launcher picks SK dividing H
+  const int n_items = a.n_seg * a.tiles_per_seg;
+  const int G = (int)gridDim.x;
+  const int my_items = (n_items - (int)blockIdx.x + G - 1) / G;
+  const int total = my_items * nk;  // stages this block streams
+  // the columns of the block's i-th item
+  auto item_tile = [&](int i, Tile& t) {
+    const int it = (int)blockIdx.x + i * G;
+    const int seg = a.seg_begin + it / a.tiles_per_seg;
+    const int jt = it % a.tiles_per_seg;
+    const int64_t col0 = (int64_t)jt * kVocabTile;
+    t.start = uni64((int64_t)seg * a.seg_len + col0);
+    t.len = uni((int)min((int64_t)kVocabTile, a.seg_len - col0));
+    t.tile0 = uni(seg * a.tiles_per_seg + jt);
+    t.row0 = 0;
+    t.rows = a.rows;
+  };
+
+  if (wave >= CW) {
+    // ---- producer: W stages into the ring ----
+    const int p = wave - CW;
+    const uint32_t lbase = (uint32_t)(uintptr_t)lds_w;
+    int i_item = 0, k_in = 0;  // next stage to issue: item, K stage
+    i32x4 desc;
+    uint32_t voff[DPW];
+    auto set_item = [&](int i) {
+      Tile t;
+      item_tile(i, t);
+      desc = buffer_desc(a.W + (t.start - a.w_row0) * (int64_t)H, (uint32_t)(t.len * H * 2));
+#pragma unroll
+      for (int d = 0; d < DPW; ++d) {
+        const int q = d * NPW + p;  // instruction q fills staged rows RPI q .. RPI q + RPI - 1
+        const int r = RPI * q + lane / (RB / 16);
+        const int c = (lane % (RB / 16)) ^ (r & 15);
+        voff[d] = (uint32_t)(min(r, t.len - 1) * H + c * 8) * 2u;
+      }
+    };
+    auto issue = [&](int g) {  // global stage g = (i_item, k_in)
+      if (k_in == 0) set_item(i_item);
+      // uniform by construction; readfirstlane keeps the asm's scalar operands in SGPRs
+      const uint32_t dst = (uint32_t)uni((int)(lbase + (uint32_t)(g % NS) * SW));
+      const uint32_t so = (uint32_t)uni(k_in * RB);
+      i32x4 du;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) du[w] = uni(desc[w]);
+#pragma unroll
+      for (int d = 0; d < DPW; ++d)
+        dma16_asm(du, dst + (uint32_t)(d * NPW + p) * 1024u, voff[d], so);
+      if (++k_in == nk) {
+        k_in = 0;
+        ++i_item;
+      }
+    };
+    const int pro = min(NS - 1, total);
+    for (int g = 0; g < pro; ++g) issue(g);
+    for (int g = 0; g < total; ++g) {
+      // stage g has landed (for this wave) once at most the younger stages are in flight
+      wait_vm_n<DPW, NS - 2>(min(NS - 2, total - 1 - g));
+      __asm__ volatile("s_barrier" ::: "memory");
+      // the slot of stage g - 1 is free: every compute wave finished it before this barrier
+      if (g + NS - 1 < total) issue(g + NS - 1);
+    }
+    return;
+  }
+
+  // ---- compute waves ----
+  const int rows = a.rows;
+  const bool has_rows = 16 * NBW * wave < rows;  // uniform: this wave owns a row of the launch
+  // hidden fragment of token block j (row 16 (NBW wave + j) + lane & 15, clamped into the launch)
+  // at K-step s of stage k: lane group lane >> 4 carries K SK k + 32 s + 8 (lane >> 4) .. +7
+  uint32_t hoff[NBW];
+#pragma unroll
+  for (int j = 0; j < NBW; ++j) {
+    const int r = min(16 * (NBW * wave + j) + (lane & 15), rows - 1);
+    hoff[j] = (uint32_t)(r * H + 8 * (lane >> 4)) * 2u;
+  }
+  const uint8_t* hbase = (const uint8_t*)a.hidden;
+  bf16x8 hb[HD + 1][KS][NBW];
+  // always issued (rows are clamped into the launch), so that the compiler's count of
+  // outstanding loads stays exact and each wait covers only the stage it needs
+  auto load_h = [&](auto slot_c, int k) __attribute__((always_inline)) {  // slot: compile-time
+    constexpr int slot = decltype(slot_c)::value;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int j = 0; j < NBW; ++j)
+        hb[slot][s][j] = *(const bf16x8*)(hbase + hoff[j] + (uint32_t)(SK * k + 32 * s) * 2u);
+  };
+  // fragment read of K-step s: row lane & 15 of a 16-row block, logical piece 4 s + (lane >> 4)
+  const int r16 = lane & 15;
+  int loff[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) loff[s] = r16 * RB + (((4 * s + (lane >> 4)) ^ r16) << 4);
+
+  f32x4 acc[4][NBW];
+  int ytgt[NBW];
+  int kp = 0;  // K stage of the next hidden prefetch
+  unroll_seq(std::make_integer_sequence<int, HD>{}, [&](auto hc) __attribute__((always_inline)) {
+    load_h(hc, kp);
+    if (++kp == nk) kp = 0;
+  });
+  int item = 0, k = 0;
+  Tile t;
+  item_tile(0, t);
+  // The stage loop, unrolled HD + 1 times so that the hidden ring's slots are compile-time.
+  auto step = [&](auto slot_c, int g) __attribute__((always_inline)) {
+    constexpr int slot = decltype(slot_c)::value;
+    if (k == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NBW; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0f;
+      // the item's targets, read now so that they have long landed at its epilogue
+      load_targets<NBW>(ytgt, a, t, wave, lane);
+    }
+    // every LDS read of the previous stage is done before its slot is handed back
+    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // hidden rows HD stages ahead (the same rows for every item: K wraps at the item's end;
+    // past the block's last stage the loads are harmless repeats)
+    load_h(std::integral_constant<int, (slot + HD) % (HD + 1)>{}, kp);
+    if (++kp == nk) kp = 0;
+    if (has_rows) {
+      const uint8_t* sp = lds_w + (g % NS) * SW;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        bf16x8 fa[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fa[i] = *(const bf16x8*)(sp + i * 16 * RB + loff[s]);
+#pragma unroll
+        for (int j = 0; j < NBW; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], hb[slot][s][j], acc[i][j],
+                                                                0, 0, 0);
+      }
+    }
+    if (++k == nk) {
+      if (has_rows) tile_epilogue<4, NBW, ENT, TEMP, PORT>(acc, ytgt, a, t, 0, wave, lane);
+      k = 0;
+      if (++item < my_items) item_tile(item, t);
+    }
+  };
+  constexpr auto seq = std::make_integer_sequence<int, HD + 1>{};
+  int g = 0;
+  for (; g + HD < total; g += HD + 1)
+    unroll_seq(seq, [&](auto sc) __attribute__((always_inline)) { step(sc, g + decltype(sc)::value); });
+  // the last stages, with their hidden-ring slots still in the same order
+  unroll_seq(seq, [&](auto sc) __attribute__((always_inline)) {
+    if (g + decltype(sc)::value < total) step(sc, g + decltype(sc)::value);
+  });
+}
+
+// --------------------------------------------------------------------------------------------
 // K2a: fold of one segment's tile partials for 64 rows (C8). Lane = row, so every load of a wave
 // is one contiguous 256-byte piece of a [tile][row] array. The block's 16 waves first take the
 // segment's tiles round-robin for the exact maximum, then its groups of 32 tiles round-robin,
 // each group one sequential chain; wave 0 then runs the pairwise tree over the groups in LDS.
+// Each wave issues all loads of a pass (up to UM maxima, a whole group) before it uses them, so a
+// pass costs one memory latency rather than one per few tiles.
+// With a.done set, the fold of the last segment to finish for a row block also runs the
+// cross-segment merge (C9, C10) of those rows, so a forward needs no separate merge launch:
+// every block publishes its records, counts itself in done[row block], and the block that
+// completes the count reads all records back and writes the outputs.
 // --------------------------------------------------------------------------------------------
 constexpr int kFoldWaves = 16;
+
+template <int NS, bool ENT, bool PORT>
+__device__ __forceinline__ void merge_row(const MergeArgs& a, int t, int32_t y);
+template <bool ENT, bool PORT>
+__device__ __forceinline__ void merge_one(const MergeArgs& a, int t);
 
 template <bool ENT, bool PORT>
 __global__ void __launch_bounds__(64 * kFoldWaves) k_segment_fold(const FoldArgs a) {
   constexpr int G = kFoldGroup;
-  constexpr int U = 8;  // loads issued ahead of the arithmetic
+  constexpr int UM = 40;  // maxima loaded per wave and pass
   __shared__ float red[kFoldWaves][64];
   __shared__ float ga[kMaxFoldGroups][64];
   __shared__ float gb[ENT ? kMaxFoldGroups : 1][64];
@@ -677,15 +897,15 @@ __global__ void __launch_bounds__(64 * kFoldWaves) k_segment_fold(const FoldArgs
   const int Q = (n + G - 1) / G;
 
   float M = -INFINITY;
-  for (int j0 = wave; j0 < n; j0 += U * kFoldWaves) {
-    float v[U];
+  for (int j0 = wave; j0 < n; j0 += UM * kFoldWaves) {
+    float v[UM];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < UM; ++u) {
       const int j = j0 + u * kFoldWaves;
       v[u] = j < n ? pm[(int64_t)j * a.ld] : -INFINITY;
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) M = fmaxf(M, v[u]);
+    for (int u = 0; u < UM; ++u) M = fmaxf(M, v[u]);
   }
   red[wave][lane] = M;
   __syncthreads();
@@ -694,26 +914,25 @@ __global__ void __launch_bounds__(64 * kFoldWaves) k_segment_fold(const FoldArgs
   for (int w = 1; w < kFoldWaves; ++w) M = fmaxf(M, red[w][lane]);
 
   for (int q = wave; q < Q; q += kFoldWaves) {
-    const int j1 = min(n, (q + 1) * G);
+    const int j0 = q * G;
+    const int len = min(n - j0, G);
+    float vm[G], vs[G], vu[ENT ? G : 1];
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const bool in = u < len;
+      const int64_t o = (int64_t)(j0 + u) * a.ld;
+      vm[u] = in ? pm[o] : 0.0f;
+      vs[u] = in ? ps[o] : 0.0f;
+      if constexpr (ENT) vu[u] = in ? pu[o] : 0.0f;
+    }
     float A = 0.0f, B = 0.0f;
-    for (int j0 = q * G; j0 < j1; j0 += U) {
-      float vm[U], vs[U], vu[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const bool in = j0 + u < j1;
-        const int64_t o = (int64_t)(j0 + u) * a.ld;
-        vm[u] = in ? pm[o] : 0.0f;
-        vs[u] = in ? ps[o] : 0.0f;
-        if constexpr (ENT) vu[u] = in ? pu[o] : 0.0f;
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (j0 + u < j1) {
-          const float dm = vm[u] - M;
-          const float e = EXP<PORT>(dm);
-          A = A + vs[u] * e;
-          if constexpr (ENT) B = B + (vu[u] + vs[u] * dm) * e;
-        }
+    for (int u = 0; u < G; ++u) {
+      if (u < len) {
+        const float dm = vm[u] - M;
+        const float e = EXP<PORT>(dm);
+        A = A + vs[u] * e;
+        if constexpr (ENT) B = B + (vu[u] + vs[u] * dm) * e;
       }
     }
     ga[q][lane] = A;
@@ -728,16 +947,30 @@ __global__ void __launch_bounds__(64 * kFoldWaves) k_segment_fold(const FoldArgs
       if constexpr (ENT) gb[q][lane] = gb[q][lane] + gb[q + st][lane];
     }
   }
-  if (!live) return;
-  const int32_t y = a.targets[t];
-  const int64_t lo = (int64_t)seg * a.seg_len;
-  const bool owner = y >= 0 && (int64_t)y >= lo && (int64_t)y < lo + a.seg_len;
-  rlk_segment_record_t r;
-  r.m = M;
-  r.s = ga[0][lane];
-  r.u = ENT ? gb[0][lane] : 0.0f;
-  r.tgt = owner ? a.tgt[t] : __builtin_nanf("");
-  a.rec[(int64_t)sl * a.rec_ld + t] = r;
+  if (live) {
+    const int32_t y = a.targets[t];
+    const int64_t lo = (int64_t)seg * a.seg_len;
+    const bool owner = y >= 0 && (int64_t)y >= lo && (int64_t)y < lo + a.seg_len;
+    rlk_segment_record_t r;
+    r.m = M;
+    r.s = ga[0][lane];
+    r.u = ENT ? gb[0][lane] : 0.0f;
+    r.tgt = owner ? a.tgt[t] : __builtin_nanf("");
+    a.rec[(int64_t)sl * a.rec_ld + t] = r;
+  }
+  if (a.done == nullptr) return;
+  // publish this segment's records device-wide, then count it for the row block
+  __threadfence();
+  uint32_t prev = 0;
+  if (lane == 0)
+    prev = __hip_atomic_fetch_add(a.done + blockIdx.x, 1u, __ATOMIC_ACQ_REL,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+  prev = (uint32_t)__builtin_amdgcn_readfirstlane((int)prev);
+  if (prev != (uint32_t)gridDim.y - 1) return;
+  // the last segment of this row block: every other block's records are visible now
+  __threadfence();
+  if (lane == 0) __hip_atomic_store(a.done + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (live) merge_one<ENT, PORT>(a.mg, t);
 }
 
 // --------------------------------------------------------------------------------------------
@@ -777,10 +1010,9 @@ __device__ __forceinline__ void merge_row(const MergeArgs& a, int t, int32_t y) 
   }
 }
 
+// Outputs of row t (C10), including padded rows and out-of-range targets.
 template <bool ENT, bool PORT>
-__global__ void __launch_bounds__(256) k_merge(const MergeArgs a) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t >= a.rows) return;
+__device__ __forceinline__ void merge_one(const MergeArgs& a, int t) {
   const int32_t y = a.targets[t];
   if (y < 0) {
     a.logp[t] = 0.0f;
@@ -802,6 +1034,13 @@ __global__ void __launch_bounds__(256) k_merge(const MergeArgs a) {
     case 4: merge_row<4, ENT, PORT>(a, t, y); break;
     default: merge_row<8, ENT, PORT>(a, t, y); break;
   }
+}
+
+template <bool ENT, bool PORT>
+__global__ void __launch_bounds__(256) k_merge(const MergeArgs a) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= a.rows) return;
+  merge_one<ENT, PORT>(a, t);
 }
 
 // --------------------------------------------------------------------------------------------
@@ -847,9 +1086,12 @@ __global__ void __launch_bounds__(256) k_rmsnorm(const RmsArgs a) {
   }
 }
 
-// Clears the status word and the LM-head work queues that follow it in its 128-byte slot.
-__global__ void k_clear_status(uint32_t* status) {
-  if (threadIdx.x < kStatusSlotWords) status[threadIdx.x] = 0u;
+// Clears the status word and the LM-head work queues that follow it in its 128-byte slot, and
+// the fused-merge counters of the segment fold.
+__global__ void k_clear_status(uint32_t* status, uint32_t* done, int64_t n_done) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < kStatusSlotWords) status[i] = 0u;
+  if (done && i < n_done) done[i] = 0u;
 }
 
 // --------------------------------------------------------------------------------------------
@@ -905,6 +1147,24 @@ static hipError_t launch_variant(const LmheadArgs& a, bool ent, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int CW, int NBW, int HD, int SK, int NS, int NPW>
+static hipError_t launch_stream(const LmheadArgs& a, bool ent, hipStream_t s) {
+  const int64_t items = (int64_t)a.n_seg * a.tiles_per_seg;
+  if (items == 0 || a.rows == 0) return hipSuccess;
+  if (a.rows > 16 * NBW * CW) return hipErrorInvalidValue;  // every row needs a compute wave
+  // as few blocks as give every block the same number of items (+-1) at the least items per
+  // block: 594 tiles on 256 CUs -> 198 blocks of 3 (not 82 of 3 and 174 of 2)
+  const int64_t cu = a.n_cu > 0 ? a.n_cu : 256;
+  const int64_t per = (items + cu - 1) / cu;
+  const int64_t blocks = (items + per - 1) / per;
+  const dim3 grid((unsigned)blocks), block(64 * (CW + NPW));
+  with_modes(a, ent, [&](auto e, auto t, auto p) {
+    hipLaunchKernelGGL((k_lmhead_stream<CW, NBW, SK, NS, NPW, HD, e.value, t.value, p.value>), grid,
+                       block, 0, s, a);
+  });
+  return hipGetLastError();
+}
+
 template <int VW, int TW, int NTB, int NS, int NTPB, int HS = 0>
 static hipError_t launch_deep(const LmheadArgs& a, bool ent, hipStream_t s) {
   constexpr int BT = 32 * NTB * TW;
@@ -936,6 +1196,15 @@ static bool three_tile_blocks(const LmheadArgs& a) {
 hipError_t launch_lmhead(const LmheadArgs& a, int bt, bool ent, hipStream_t s) {
   if (bt == 0) {
     if (a.rows > 256) return launch_variant<2, 4, 2>(a, ent, s);
+    // up to 32 rows: the W stream alone bounds the launch (streaming kernel, measured 57 us
+    // per 311 MB vocab segment against 67 us for 3-tile blocks); more rows: 3-tile blocks
+    if (a.rows <= 32) {
+      if (a.H % 256 == 0) {
+        if (a.rows <= 16) return launch_stream<1, 1, 2, 256, 4, 4>(a, ent, s);
+        return launch_stream<2, 1, 2, 256, 4, 4>(a, ent, s);
+      }
+      return launch_stream<2, 1, 3, 128, 8, 2>(a, ent, s);
+    }
     if (three_tile_blocks(a)) {
       if (a.rows > 192) return launch_deep<3, 4, 2, 3, 3, 2>(a, ent, s);
       if (a.rows > 128) return launch_deep<3, 2, 3, 3, 3>(a, ent, s);
@@ -987,8 +1256,10 @@ hipError_t launch_rmsnorm(const RmsArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_clear_status(uint32_t* status, hipStream_t s) {
-  hipLaunchKernelGGL(k_clear_status, dim3(1), dim3(64), 0, s, status);
+hipError_t launch_clear_status(uint32_t* status, uint32_t* done, int64_t n_done, hipStream_t s) {
+  const int64_t n = std::max<int64_t>(kStatusSlotWords, done ? n_done : 0);
+  hipLaunchKernelGGL(k_clear_status, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, status,
+                     done, n_done);
   return hipGetLastError();
 }
 

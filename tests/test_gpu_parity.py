@@ -58,6 +58,9 @@ SHAPES = [
     (513, 384, 3000, 2, 0.7, True),    # 2 segments of 1500 = 23 tiles + 28, temperature
     (33, 1024, 1000, 1, 1.0, False),   # one segment, 15 full tiles + 40
     (1, 128, 4000, 8, 1.0, True),      # a single row, 8 segments of 500 = 7 tiles + 52
+    (16, 256, 5000, 2, 0.7, True),     # <= 16 rows (streaming kernel), temperature
+    (27, 640, 3000, 4, 1.0, True),     # 17..32 rows, H not a multiple of 256 (128-K stages)
+    (32, 1024, 151936, 4, 1.0, False), # 32 rows over 4 x 594 tiles (3 items per streaming block)
     (1030, 128, 768, 4, 1.3, True),    # many row tiles, segments of 3 tiles (blocks of 4 with one absent)
     (40, 128, 516, 4, 1.0, True),      # segments of 129 = 2 tiles + a 1-column tile
     (70, 128, 160, 8, 1.0, False),     # segments of 20 columns: one partial tile each
