@@ -377,7 +377,15 @@ def time_layout(rlk, lp, hd, Wd, yd, gd, T, steps, warmup, layout_kw, flops_per_
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    # the step as a caller runs it: no events inside
     ev = HipEvents(2 + 2 * n_launch * steps)
+    ev.record(0, sp)
+    for _ in range(steps):
+        step()
+    ev.record(1, sp)
+    torch.cuda.synchronize()
+    plain = ev.ms(0, 1)
+    # the same steps with events around every LM-head launch (the kernels' own time)
     ev.record(0, sp)
     for i in range(steps):
         base = 2 + 2 * n_launch * i
@@ -388,62 +396,129 @@ def time_layout(rlk, lp, hd, Wd, yd, gd, T, steps, warmup, layout_kw, flops_per_
     kern = sum(ev.ms(2 + 2 * j, 3 + 2 * j) for j in range(n_launch * steps))
     ev.close()
     del keep
-    return {"ms_per_step": total / steps, "lmhead_ms_per_step": kern / steps,
-            "lmhead_launches_per_step": n_launch, "_logp": logp.cpu().numpy().copy()}
+    return {"ms_per_step": plain / steps, "ms_per_step_with_launch_events": total / steps,
+            "lmhead_ms_per_step": kern / steps, "lmhead_launches_per_step": n_launch,
+            "_logp": logp.cpu().numpy().copy()}
 
 
-def torch_native(np, torch, hd, Wd, yd, sizes, ref_logp, steps: int = 5, warmup: int = 2) -> dict:
-    """The same rows through a plain framework LM head, for attribution: bf16 logits from the
-    vendor GEMM (``F.linear``, hipBLASLt), then fp32 log_softmax and a gather. Reports its step
-    time, how far it is from this library's output, and whether it keeps its bits when the rows
-    arrive as the rollout's decode batches instead of one pass (each batch its own GEMM)."""
+def p_head(torch, h, W, y, sizes=None, shards: int = 1):
+    """P, the production/native path of the ablation matrix: a plain framework LM head. Training
+    layout (sizes None, one shard): bf16 logits from the vendor GEMM (``F.linear``, hipBLASLt),
+    fp32 log_softmax, gather. Rollout layout: each decode batch on its own, with W split into
+    `shards` contiguous row ranges as a TP rollout holds it: every shard's bf16 logits, their
+    fp32 max and sum of exp, then the shards merged the way a vocab-parallel log-softmax merges
+    them (global max, rescaled sum) and the target's logit taken from its shard. Padded rows
+    give 0. Returns fp32 logp [T]."""
+    T = int(h.shape[0])
+    V = int(W.shape[0])
+    yl = y.long()
+    active = yl >= 0
+    yc = yl.clamp_min(0)
+    if sizes is None and shards == 1:
+        z = torch.nn.functional.linear(h, W).float()
+        lp = torch.log_softmax(z, dim=-1).gather(1, yc[:, None])[:, 0]
+        return torch.where(active, lp, torch.zeros_like(lp))
+    sizes = [T] if sizes is None else sizes
+    L = V // shards
+    out = []
+    r0 = 0
+    for n in sizes:
+        rows = slice(r0, r0 + n)
+        ms, ss, zy = [], [], torch.zeros(n, dtype=torch.float32, device=h.device)
+        for sh in range(shards):
+            z = torch.nn.functional.linear(h[rows], W[sh * L:(sh + 1) * L]).float()
+            m = z.max(dim=-1).values
+            ms.append(m)
+            ss.append(torch.exp(z - m[:, None]).sum(dim=-1))
+            own = (yc[rows] >= sh * L) & (yc[rows] < (sh + 1) * L)
+            loc = (yc[rows] - sh * L).clamp(0, L - 1)
+            zy = torch.where(own, z.gather(1, loc[:, None])[:, 0], zy)
+        M = torch.stack(ms).max(dim=0).values
+        S = (torch.stack(ss) * torch.exp(torch.stack(ms) - M[None, :])).sum(dim=0)
+        lp = zy - (M + torch.log(S))
+        out.append(torch.where(active[rows], lp, torch.zeros_like(lp)))
+        r0 += n
+    return torch.cat(out)
+
+
+def ablation_matrix(rlk, np, torch, lp, hd, Wd, yd, sizes, shards: int = 4, ref=None,
+                    reps: int = 3) -> dict:
+    """The selected-logprob ablation matrix in the pages' four cells (vime issue #45, matrix
+    semantics and report fields): the training side computes the rows in one pass, the rollout
+    side as the decode batches over `shards` vocab shards; R is this library, P the plain
+    framework head (p_head). Cell "X/Y" = training X, rollout Y. Each cell reports the
+    training-vs-rollout comparison of the same rows (mismatch_count over raw bits, max_abs_diff,
+    logprob_abs_diff_{mean,max,p50,p90,p99} over active rows), both sides' wall times (mean of
+    `reps` runs, inputs resident on the GPU), and, given the oracle's logp of every row (`ref`),
+    each side's distance to it. R/R is the strict baseline and is never left out."""
     h = hd.view(torch.bfloat16)
     W = Wd.view(torch.bfloat16)
-    y = yd.long()
-    active = y >= 0
+    act = (yd >= 0).cpu().numpy()
 
-    def run(rows: slice):
-        z = torch.nn.functional.linear(h[rows], W).float()
-        lp = torch.log_softmax(z, dim=-1).gather(1, y[rows].clamp_min(0)[:, None])[:, 0]
-        return torch.where(active[rows], lp, torch.zeros_like(lp))
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            out = fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return out.cpu().numpy().copy(), e0.elapsed_time(e1) / reps
 
+    runs = {
+        ("R", "training"): lambda: lp.forward(hd, Wd, yd)["logp"],
+        ("R", "rollout"): lambda: lp.forward(hd, Wd, yd, batch_sizes=sizes,
+                                             vocab_shards=shards)["logp"],
+        ("P", "training"): lambda: p_head(torch, h, W, yd),
+        ("P", "rollout"): lambda: p_head(torch, h, W, yd, sizes, shards),
+    }
+    res = {k: timed(f) for k, f in runs.items()}
+    impl = {"R": "rlk_logprob (HIP, gfx950)",
+            "P": "F.linear bf16 logits (hipBLASLt) + fp32 log_softmax + gather"}
+    cells = {}
+    for tr, ro in (("R", "R"), ("P", "R"), ("R", "P"), ("P", "P")):
+        a, ta = res[(tr, "training")]
+        b, tb = res[(ro, "rollout")]
+        c = {"requested_case": f"{tr}/{ro}", "actual_training_implementation": impl[tr],
+             "actual_rollout_implementation": impl[ro], "fallbacks": [],
+             "active_token_count": int(act.sum()),
+             "mismatch_count": int(np.count_nonzero(a.view(np.uint32) != b.view(np.uint32))),
+             "max_abs_diff": float(np.max(np.abs(a.astype(np.float64) - b.astype(np.float64)))),
+             **diff_stats(a[act], b[act]),
+             "training_wall_time_ms": ta, "rollout_wall_time_ms": tb,
+             "step_wall_time_ms": ta + tb}
+        if ref is not None:
+            c["training_vs_oracle_max"] = float(np.max(np.abs(a[act] - ref[act])))
+            c["rollout_vs_oracle_max"] = float(np.max(np.abs(b[act] - ref[act])))
+        cells[f"{tr}/{ro}"] = c
+    return {"training_layout": "one pass",
+            "rollout_layout": f"{len(sizes)} decode batches x {shards} vocab shards",
+            "cells": cells, "_logp": {f"{k[0]}_{k[1]}": v[0] for k, v in res.items()}}
+
+
+def vendor_gemm_ms(torch, hd, Wd, steps: int = 5, warmup: int = 2) -> float:
+    """The vendor GEMM alone at the head's shape (bf16 logits, no log-softmax): the same
+    contraction without the fused epilogue, on the same box and operands."""
+    h = hd.view(torch.bfloat16)
+    W = Wd.view(torch.bfloat16)
     for _ in range(warmup):
-        run(slice(None))
+        torch.nn.functional.linear(h, W)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(steps):
-        one = run(slice(None))
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
-    # the vendor GEMM alone (bf16 logits, no log-softmax): the same contraction without the
-    # fused epilogue, on the same box and the same operands
-    for _ in range(warmup):
-        torch.nn.functional.linear(h, W)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(steps):
         torch.nn.functional.linear(h, W)
     e1.record()
     torch.cuda.synchronize()
-    gemm_ms = e0.elapsed_time(e1) / steps
-    one_h = one.cpu().numpy()
-    offs = np.concatenate([[0], np.cumsum(sizes)])
-    parts = [run(slice(int(offs[i]), int(offs[i + 1]))) for i in range(len(sizes))]
-    torch.cuda.synchronize()
-    dec = torch.cat(parts).cpu().numpy()
-    T = int(h.shape[0])
-    return {"what": "F.linear (bf16 logits) + fp32 log_softmax + gather",
-            "ms_per_step": ms, "tokens_per_s": int(active.sum().item()) / (ms * 1e-3),
-            "vendor_gemm_only_ms": gemm_ms,
-            "vendor_gemm_only_frac_of_bf16_peak":
-                2.0 * h.shape[0] * h.shape[1] * W.shape[0] / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-            "mismatch_count_decode_batches_vs_one_pass": int(np.count_nonzero(
-                dec.view(np.uint32) != one_h.view(np.uint32))),
-            "rows": T, "max_abs_diff_vs_this_library": float(np.max(np.abs(
-                one_h.astype(np.float64) - ref_logp.astype(np.float64)))),
-            "_logp": one_h}
+    return e0.elapsed_time(e1) / steps
+
+
+def reference_logp(np, name: str):
+    """The oracle's logp of every row of a workload, as stored in tests/golden (written by
+    tests/golden/make_reference.py from the oracle alone), or None when absent."""
+    f = os.path.join(ROOT, "tests", "golden", f"reference_{name}.npy")
+    return np.load(f, allow_pickle=False)[0] if os.path.exists(f) else None
 
 
 def long_grpo(rlk, datagen, np, torch, Wd) -> dict:
@@ -518,7 +593,9 @@ def rollout(rlk, datagen, np, hd, Wd, yd, w, ref_logp, steps: int = 3, warmup: i
     res = {
         "decode_batches": len(sizes), "lmhead_launches_per_step": r["lmhead_launches_per_step"],
         "ms_per_step": r["ms_per_step"], "tokens_per_s": w.T / (r["ms_per_step"] * 1e-3),
+        "ms_per_step_with_launch_events": r["ms_per_step_with_launch_events"],
         "lmhead_ms_per_step": r["lmhead_ms_per_step"],
+        "outside_lmhead_ms_per_step": r["ms_per_step"] - r["lmhead_ms_per_step"],
         "w_stream_GBps": w_bytes / (r["lmhead_ms_per_step"] * 1e-3) / 1e9,
         "hbm_frac": w_bytes / (r["lmhead_ms_per_step"] * 1e-3) / 8e12}
     if ref_logp is not None:
@@ -548,8 +625,15 @@ def extras(rlk, datagen, np, torch, hd, Wd, yd, w, ref_logp) -> dict:
     del lpp
     log("extras: backward")
     out["backward_one_pass"] = backward(rlk, np, torch, hd, Wd, yd, w)
-    log("extras: torch-native reference path")
-    out["torch_native_lm_head"] = torch_native(np, torch, hd, Wd, yd, sizes, ref_logp)
+    log("extras: ablation matrix (R = this library, P = plain framework head)")
+    lp = rlk.Logprob(w.H, w.V, vocab_segments=w.segments, device=0)
+    ab = ablation_matrix(rlk, np, torch, lp, hd, Wd, yd, sizes, 4, reference_logp(np, w.name))
+    ab.pop("_logp")
+    out["ablation_matrix"] = ab
+    gms = vendor_gemm_ms(torch, hd, Wd)
+    out["vendor_gemm_only"] = {
+        "what": "F.linear at the head's shape, bf16 logits, no log-softmax", "ms": gms,
+        "frac_of_bf16_peak": 2.0 * w.T * w.H * w.V / (gms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
     log("extras: long_grpo inputs")
     out["long_grpo"] = long_grpo(rlk, datagen, np, torch, Wd)
     wn = datagen.WORKLOADS["norm_head"]
@@ -733,10 +817,6 @@ def main() -> int:
         result["cpu_baseline"] = cb
         result["oracle_max_abs_diff_on_sample"] = float(np.max(np.abs(
             out_logp[rows].astype(np.float64) - ref)))
-        tn = result.get("extras", {}).get("torch_native_lm_head")
-        if tn is not None:
-            tn["max_abs_diff_vs_oracle_on_sample"] = float(np.max(np.abs(
-                tn["_logp"][rows].astype(np.float64) - ref)))
     else:
         result["cpu_baseline"] = None
     # the report record of the run (requested case, fingerprints, fallbacks, diffs to the oracle)
@@ -747,14 +827,15 @@ def main() -> int:
            "active_token_count": active, "mismatch_count": mismatch,
            "tokens_per_second": value,
            "peak_memory_bytes": int(torch.cuda.max_memory_allocated())}
-    if not args.no_cpu_baseline:
+    full = reference_logp(np, args.workload)
+    if full is not None:
+        # every active row against the oracle's stored outputs
+        rep["vs_oracle"] = diff_stats(out_logp[y >= 0], full[y >= 0])
+    elif not args.no_cpu_baseline:
         rep["vs_oracle"] = diff_stats(out_logp[rows], ref)
-        tn = result.get("extras", {}).get("torch_native_lm_head")
-        if tn is not None:
-            rep["torch_native_vs_oracle"] = diff_stats(tn["_logp"][rows], ref)
+    if "ablation_matrix" in result.get("extras", {}):
+        rep["ablation_matrix"] = result["extras"]["ablation_matrix"]["cells"]
     result["report"] = rep
-    if "torch_native_lm_head" in result.get("extras", {}):
-        result["extras"]["torch_native_lm_head"].pop("_logp")
     print(json.dumps(result), flush=True)
     del keep
     return 0

@@ -1,6 +1,8 @@
 """The full-size workloads, in the launch configuration bench.py times (one pass) and in every
-rollout/training layout they name. Parity against the float64 oracle is checked on sampled rows
-the oracle computes one by one; layout invariance on every row, byte for byte.
+rollout/training layout they name. Parity against the float64 oracle is checked on every row,
+against the oracle's outputs stored in tests/golden (reference_<workload>.npy, written by
+make_reference.py from the oracle alone and tied to the input bytes by sha256), and on sampled
+rows the oracle recomputes here; layout invariance on every row, byte for byte.
 """
 
 import numpy as np
@@ -8,8 +10,8 @@ import pytest
 
 import datagen
 import oracle
-from tests.helpers import (assert_bitwise, dev_bits, dev_i32, diff_stats, golden_targets, host,
-                           say)
+from tests.helpers import (GOLDEN, assert_bitwise, dev_bits, dev_i32, diff_stats, golden_targets,
+                           host, say)
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-3
@@ -29,6 +31,37 @@ def head_inputs():
 @pytest.fixture(scope="module")
 def W64(head_inputs):
     return oracle.bf16_bits_to_f64(head_inputs[2])
+
+
+def _reference(name, h, Wb, y, gamma=None):
+    """The oracle's logp, lse and entropy of every row of a workload, stored with the sha256 of
+    the inputs and targets they were computed from (checked here)."""
+    import json
+    import os
+
+    ref = np.load(os.path.join(GOLDEN, f"reference_{name}.npy"), allow_pickle=False)
+    with open(os.path.join(GOLDEN, f"reference_{name}.json")) as f:
+        meta = json.load(f)
+    assert meta["sha256_hidden"] == datagen.sha256(h), "reference belongs to other hidden bytes"
+    assert meta["sha256_W"] == datagen.sha256(Wb), "reference belongs to another W"
+    assert meta["sha256_targets"] == datagen.sha256(y), "reference belongs to other targets"
+    if gamma is not None:
+        assert meta["sha256_gamma"] == datagen.sha256(gamma)
+    assert meta["sha256_values"] == datagen.sha256(ref)
+    return {"logp": ref[0], "lse": ref[1], "entropy": ref[2]}
+
+
+def _parity_all(got, ref, y, keys=("logp", "lse")):
+    """Every active row within 1e-3 of the oracle; padded rows exactly +0.0. Prints the
+    logprob_abs_diff_{mean,max,p50,p90,p99} report fields."""
+    act = y >= 0
+    for k in keys:
+        s = diff_stats(got[k], ref[k], act)
+        print(f"{k}: " + ", ".join(f"{k}_abs_diff_{q}={s[q]:.3e}"
+                                     for q in ("mean", "max", "p50", "p90", "p99"))
+              + f" over {s['n']} active rows", flush=True)
+        assert s["max"] <= TOL, (k, s)
+        assert np.all(got[k][~act] == 0.0) and not np.any(np.signbit(got[k][~act])), k
 
 
 def _sample(n_rows, k, active):
@@ -54,6 +87,7 @@ def test_qwen3_head_one_pass_matches_oracle_on_sampled_rows(rlk, head_inputs, W6
     torch.cuda.synchronize()
     got = {k: host(out[k]) for k in ("logp", "lse")}
     assert np.all(got["logp"] <= 0.0) and np.all(np.isfinite(got["logp"]))
+    _parity_all(got, _reference("qwen3_8b_head", h, Wb, y), y)
     _parity(got, h, W64, y, _sample(w.T, 32, y >= 0))
 
 
@@ -67,6 +101,7 @@ def test_qwen3_head_training_vs_rollout_layouts(rlk, head_inputs):
     decode = datagen.decode_layout(w.T)
     for lay in (dict(row_chunk=1024), dict(row_chunk=2047), dict(batch_sizes=decode),
                 dict(vocab_shards=2), dict(vocab_shards=4),
+                dict(batch_sizes=decode, vocab_shards=2),
                 dict(batch_sizes=decode, vocab_shards=4), dict(token_tile=128)):
         say(f"qwen3_8b_head layout {({k: (len(v) if k == 'batch_sizes' else v) for k, v in lay.items()})}")
         o = lp.forward(hd, Wd, yd, **lay)
@@ -171,6 +206,7 @@ def test_long_grpo_chunkings_and_padding(rlk, head_inputs):
     for k in ("logp", "lse"):
         assert_bitwise(host(o[k]), one_h[k], (k, "nan pads"))
     del hn, hd
+    _parity_all(one_h, _reference("long_grpo", h, Wb, y), y)
     W64 = oracle.bf16_bits_to_f64(Wb)
     _parity(one_h, h, W64, y, _sample(w.T, 16, ~pad))
 
@@ -200,6 +236,7 @@ def test_norm_head_one_pass_chunks_shards(rlk):
         for k in keys:
             assert_bitwise(host(o[k]), one_h[k], (k, str(lay)))
     del xd
+    _parity_all(one_h, _reference("norm_head", x, Wb, y, g), y, keys)
     W64 = oracle.bf16_bits_to_f64(Wb)
     rows = _sample(w.T, 16, y >= 0)
     _parity(one_h, x, W64, y, rows, keys, tau=w.tau, gamma_bits=g, rms_eps=w.rms_eps)

@@ -22,6 +22,7 @@ def _layouts(T, ragged):
         dict(batch_sizes=ragged),
         dict(vocab_shards=2),
         dict(vocab_shards=4),
+        dict(batch_sizes=ragged, vocab_shards=2),
         dict(batch_sizes=ragged, vocab_shards=4),
         dict(row_chunk=7),
         dict(token_tile=32),
