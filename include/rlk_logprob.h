@@ -152,6 +152,28 @@ rlk_status_t rlk_logprob_forward_timed(rlk_logprob_t handle, const void* hidden,
                                        rlk_stream_t stream, void* const* events,
                                        int32_t num_events);
 
+/* ---- Allocation-free forward ----------------------------------------------------------------
+ * For callers that cannot allocate device memory: code being captured into a HIP graph, tight
+ * serving loops, harnesses that forbid hipMalloc. rlk_logprob_forward with the same arguments
+ * and results (bit for bit), except that the workspace is a fixed array in device memory that
+ * the library holds, one per GPU, RLK_NOALLOC_SCRATCH_BYTES (64 MiB) large, present from library
+ * load until the process ends. Nothing is allocated: no hipMalloc, hipFree or allocating library
+ * call; the caller still passes inputs and outputs.
+ *  - A layout whose rlk_logprob_workspace_size exceeds RLK_NOALLOC_SCRATCH_BYTES is refused with
+ *    RLK_ERR_WORKSPACE before anything is enqueued (about 19 KB per row at V = 151936 with four
+ *    segments, 28.5 KB with entropy: some 3400 / 2300 rows per call).
+ *  - Every call on one GPU uses that GPU's one array, and the array keeps the last call's
+ *    contents (the forward clears what must start at zero itself). Calls that overlap in time on
+ *    one GPU race: order them (one stream, or events) even across handles.
+ *  - The device status word of these calls lives in that array, not in a caller workspace, so
+ *    rlk_logprob_device_status cannot read it; a target >= V still writes NaN for its row. */
+#define RLK_NOALLOC_SCRATCH_BYTES (64u << 20)
+rlk_status_t rlk_logprob_forward_noalloc(rlk_logprob_t handle, const void* hidden,
+                                         const void* W_lm, const int32_t* targets,
+                                         const rlk_layout_desc_t* layout, const void* rms_gamma,
+                                         float* logp, float* lse, float* entropy,
+                                         rlk_stream_t stream);
+
 /* Host-only: workspace bytes of rlk_logprob_partials for `num_rows` rows over the vocab range
  * [vocab_begin, vocab_end). */
 rlk_status_t rlk_logprob_partials_workspace_size(const rlk_logprob_config_t* config,

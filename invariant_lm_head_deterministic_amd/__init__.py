@@ -34,6 +34,7 @@ from ._lib import (  # noqa: F401
     rlk_logprob_destroy,
     rlk_logprob_device_status,
     rlk_logprob_forward,
+    rlk_logprob_forward_noalloc,
     rlk_logprob_forward_timed,
     rlk_logprob_merge,
     rlk_logprob_partials,

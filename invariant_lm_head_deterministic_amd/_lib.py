@@ -79,6 +79,8 @@ _SIGS = {
     "rlk_logprob_forward_timed": (_ST, [_H, _P, _P, _P, ctypes.POINTER(rlk_layout_desc_t), _P, _P,
                                         _P, _P, _P, ctypes.c_size_t, _S,
                                         ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]),
+    "rlk_logprob_forward_noalloc": (_ST, [_H, _P, _P, _P, ctypes.POINTER(rlk_layout_desc_t), _P,
+                                          _P, _P, _P, _S]),
     "rlk_logprob_partials_workspace_size": (_ST, [ctypes.POINTER(rlk_logprob_config_t),
                                                   ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                                   ctypes.POINTER(ctypes.c_size_t)]),
@@ -192,6 +194,13 @@ def rlk_logprob_forward_timed(handle, hidden, W_lm, targets, layout, rms_gamma, 
                                            rms_gamma, logp, lse, entropy, workspace,
                                            workspace_bytes, stream, arr, len(events)),
           "rlk_logprob_forward_timed")
+
+
+def rlk_logprob_forward_noalloc(handle, hidden, W_lm, targets, layout, rms_gamma, logp, lse,
+                                entropy, stream) -> None:
+    check(load().rlk_logprob_forward_noalloc(handle, hidden, W_lm, targets, ctypes.byref(layout),
+                                             rms_gamma, logp, lse, entropy, stream),
+          "rlk_logprob_forward_noalloc")
 
 
 def rlk_logprob_partials_workspace_size(config, num_rows, vocab_begin, vocab_end) -> int:

@@ -14,6 +14,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -31,7 +32,16 @@ struct rlk_logprob {
   int device;
   int n_cu;  // compute units of the device
   std::string contract;
+  void* scratch;  // device address of this device's scratch array (allocation-free forward)
 };
+
+// The workspace of rlk_logprob_forward_noalloc: a fixed array in device memory, one copy per GPU
+// the library is loaded on, held until the process ends. In host code its name is only a
+// stand-in, never a device address: the address is resolved with hipGetSymbolAddress, once per
+// device, with that device current, and only that address is handed to kernels.
+constexpr size_t kScratchBytes = (size_t)64 << 20;  // RLK_NOALLOC_SCRATCH_BYTES
+static_assert(kScratchBytes == RLK_NOALLOC_SCRATCH_BYTES, "header and library agree");
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 namespace {
 
@@ -200,6 +210,27 @@ rlk_status_t hip_fail(hipError_t e, const char* what) {
   return fail(RLK_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices];  // per device, resolved once
+
+// The device address of `device`'s scratch array; the device must be current.
+rlk_status_t resolve_scratch(int device, void** out) {
+  *out = nullptr;
+  if (device < 0 || device >= kMaxScratchDevices)
+    return fail(RLK_ERR_NO_DEVICE, "device %d: no scratch slot (at most %d devices)", device,
+                kMaxScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[device] = p;
+  }
+  *out = g_scratch_ptr[device];
+  return RLK_OK;
+}
+
 // RMSNorm (optional) then the LM-head tile kernel over rows [r0, r1) and segments [s0, s1).
 rlk_status_t run_rows(const rlk_logprob* h, const Geometry& g, const void* hidden, const void* W,
                       int64_t w_row0, const int32_t* targets, const void* gamma, const WsMap& m,
@@ -297,11 +328,19 @@ RLK_API rlk_status_t rlk_logprob_create(const rlk_logprob_config_t* config, int 
   if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
   if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
     return fail(RLK_ERR_UNSUPPORTED_ARCH, "device %d is %s, not gfx950", device, prop.gcnArchName);
+  void* scr = nullptr;
+  {
+    DeviceGuard guard(device);
+    if (guard.err != hipSuccess) return hip_fail(guard.err, "hipSetDevice");
+    st = resolve_scratch(device, &scr);
+    if (st != RLK_OK) return st;
+  }
   rlk_logprob* h = new (std::nothrow) rlk_logprob;
   if (!h) return fail(RLK_ERR_INVALID_ARGUMENT, "out of host memory");
   h->cfg = *config;
   h->device = device;
   h->n_cu = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
+  h->scratch = scr;
   uint32_t itb;
   std::memcpy(&itb, &config->inv_temperature, 4);
   uint32_t epsb;
@@ -483,6 +522,25 @@ RLK_API rlk_status_t rlk_logprob_forward_timed(rlk_logprob_t h, const void* hidd
     return fail(RLK_ERR_INVALID_ARGUMENT, "events must hold num_events >= 0 entries");
   return forward_impl(h, hidden, W_lm, targets, layout, rms_gamma, logp, lse, entropy, workspace,
                       workspace_bytes, stream, events, num_events);
+}
+
+RLK_API rlk_status_t rlk_logprob_forward_noalloc(rlk_logprob_t h, const void* hidden,
+                                                 const void* W_lm, const int32_t* targets,
+                                                 const rlk_layout_desc_t* layout,
+                                                 const void* rms_gamma, float* logp, float* lse,
+                                                 float* entropy, rlk_stream_t stream) {
+  if (!h) return fail(RLK_ERR_INVALID_ARGUMENT, "handle is NULL");
+  size_t need = 0;
+  rlk_status_t st = rlk_logprob_workspace_size(&h->cfg, layout, &need);
+  if (st != RLK_OK) return st;
+  if (need > kScratchBytes)
+    return fail(RLK_ERR_WORKSPACE,
+                "this forward needs %zu bytes of workspace; the allocation-free entry point has "
+                "%zu (use rlk_logprob_forward with a caller workspace, or fewer rows per call)",
+                need, kScratchBytes);
+  if (!h->scratch) return fail(RLK_ERR_WORKSPACE, "no device scratch for device %d", h->device);
+  return forward_impl(h, hidden, W_lm, targets, layout, rms_gamma, logp, lse, entropy, h->scratch,
+                      kScratchBytes, stream, nullptr, 0);
 }
 
 RLK_API rlk_status_t rlk_logprob_partials_workspace_size(const rlk_logprob_config_t* config,
