@@ -68,6 +68,13 @@ typedef enum rlk_status {
   RLK_ERR_CONTRACT = 7,         /* shard range not on segment boundaries, flags mismatch */
   RLK_ERR_HIP = 8               /* a HIP runtime call failed (message in rlk_last_error) */
 } rlk_status_t;
+/* Deliberate limits of this build:
+ *  - H must be a multiple of 128 (not merely of the MFMA's 32): every kernel stages K in steps of
+ *    64 and peels its last two steps, which keeps the K loops free of remainder code. Other H
+ *    are refused with RLK_ERR_UNSUPPORTED_SHAPE, never run a second way.
+ *  - There is no separate "build failed" status: the library is a prebuilt gfx950 code object,
+ *    so a missing or foreign build fails to load (the binding refuses to run without it), and a
+ *    device that is not gfx950 gets RLK_ERR_UNSUPPORTED_ARCH at rlk_logprob_create. */
 
 /* rlk_logprob_config_t.flags */
 #define RLK_FLAG_RMSNORM 1u /* apply the final RMSNorm (rms_gamma, rms_eps) to hidden first */
@@ -132,7 +139,11 @@ rlk_status_t rlk_logprob_workspace_size(const rlk_logprob_config_t* config,
 rlk_status_t rlk_layout_check(const rlk_logprob_config_t* config,
                               const rlk_layout_desc_t* layout, int64_t* num_launches);
 
-/* The strict-path forward. hidden: bf16 [T,H]; W_lm: bf16 [V,H]; targets: int32 [T];
+/* The strict-path forward: the LM-head projection, log-softmax over the vocabulary and the
+ * target token's logprob (nxbn.cn blog §3.1; the "Linear logprob" row of the strict-path
+ * boundary table on the RL-Kernel v0.1.0 summary page), recomputed from hidden states and tokens
+ * (nxbn.cn blog §3.3), optionally after the final RMSNorm (the same table's "RMSNorm" row).
+ * hidden: bf16 [T,H]; W_lm: bf16 [V,H]; targets: int32 [T];
  * rms_gamma: bf16 [H] with RLK_FLAG_RMSNORM, else NULL. Outputs fp32 [T]: logp, lse, and
  * entropy (required with RLK_FLAG_ENTROPY, else NULL). workspace: device memory of at least
  * rlk_logprob_workspace_size bytes, 256-byte aligned; its contents on entry do not matter. */
@@ -180,8 +191,10 @@ rlk_status_t rlk_logprob_partials_workspace_size(const rlk_logprob_config_t* con
                                                  int64_t num_rows, int64_t vocab_begin,
                                                  int64_t vocab_end, size_t* bytes);
 
-/* One vocab shard's local reduction: W_shard is bf16 [vocab_end - vocab_begin, H], the rows
- * [vocab_begin, vocab_end) of W_lm; the range must start and end on segment boundaries
+/* One vocab shard's local reduction (the "actual vocab range", "target ownership" and "local
+ * reduction" of the "Linear logprob" boundary row on the RL-Kernel v0.1.0 summary page, as one
+ * rank of its TP4 rollout would compute them): W_shard is bf16 [vocab_end - vocab_begin, H],
+ * the rows [vocab_begin, vocab_end) of W_lm; the range must start and end on segment boundaries
  * (multiples of V / S_c), else RLK_ERR_CONTRACT. Writes records[(s - s0) * num_rows + t] for
  * every segment s of the range (s0 = vocab_begin / (V / S_c)) and every row t. */
 rlk_status_t rlk_logprob_partials(rlk_logprob_t handle, const void* hidden, const void* W_shard,
@@ -190,7 +203,9 @@ rlk_status_t rlk_logprob_partials(rlk_logprob_t handle, const void* hidden, cons
                                   const void* rms_gamma, rlk_segment_record_t* records,
                                   void* workspace, size_t workspace_bytes, rlk_stream_t stream);
 
-/* Cross-segment merge in the contract's fixed order: records holds S_c * num_rows records,
+/* Cross-segment merge in the contract's fixed order (the "cross-rank LSE merge" of the "Linear
+ * logprob" boundary row and the cross-TP vocab merge of the ROCm fixes list, RL-Kernel v0.1.0
+ * summary page): records holds S_c * num_rows records,
  * segment-major (all segments of the vocabulary, gathered from every shard). Writes logp, lse
  * and (with RLK_FLAG_ENTROPY) entropy. status: device uint32 that receives the
  * RLK_DEVICE_STATUS_* bits (OR-ed in), or NULL. */

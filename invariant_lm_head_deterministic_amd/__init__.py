@@ -100,6 +100,19 @@ def _ptr(t) -> int | None:
     return None if t is None else t.data_ptr()
 
 
+def _on_stream(s, dev, *tensors) -> None:
+    """Tensors the binding allocated from torch's caching allocator on the current stream but
+    handed to work enqueued on another stream `s`: record that use, so that the allocator does not
+    hand their memory out again before the work on `s` is done."""
+    import torch
+
+    if s == torch.cuda.current_stream(dev):
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(s)
+
+
 class Logprob:
     """A handle of the C library bound to one device and one numeric configuration."""
 
@@ -196,6 +209,7 @@ class Logprob:
                             layout, _ptr(gamma), out["logp"].data_ptr(), out["lse"].data_ptr(),
                             _ptr(out.get("entropy")), workspace.data_ptr(),
                             workspace.numel() * workspace.element_size(), s.cuda_stream)
+        _on_stream(s, dev, workspace, *out.values())
         del keep
         res = dict(out)  # the caller's dict is left as it was given
         res["_workspace"] = workspace
@@ -234,6 +248,7 @@ class Logprob:
         rlk_logprob_partials(self.handle, hidden.data_ptr(), W_shard.data_ptr(), vocab_begin,
                              vocab_end, targets.data_ptr(), T, _ptr(gamma), records.data_ptr(),
                              ws.data_ptr(), ws.numel(), s.cuda_stream)
+        _on_stream(s, dev, ws, records)
         return records
 
     def backward(self, hidden, W, targets, lse, grad_logp, *, entropy=None, grad_entropy=None,
@@ -297,6 +312,7 @@ class Logprob:
                              _ptr(out.get("grad_W")), _ptr(out.get("grad_gamma")),
                              RLK_BWD_ACCUMULATE if accumulate else 0, row_chunk,
                              workspace.data_ptr(), workspace.numel(), s.cuda_stream)
+        _on_stream(s, dev, workspace, *out.values())
         out["_workspace"] = workspace
         return out
 
@@ -348,6 +364,7 @@ class Logprob:
                                       _ptr(out.get("grad_W_shard")),
                                       RLK_BWD_ACCUMULATE if accumulate else 0, row_chunk,
                                       ws.data_ptr(), ws.numel(), s.cuda_stream)
+        _on_stream(s, dev, ws, *out.values())
         out["_workspace"] = ws
         return out
 
@@ -385,6 +402,7 @@ class Logprob:
                                    out["grad_hidden"].data_ptr(), _ptr(out.get("grad_gamma")),
                                    RLK_BWD_ACCUMULATE if accumulate else 0, ws.data_ptr(),
                                    ws.numel(), s.cuda_stream)
+        _on_stream(s, dev, ws, *out.values())
         out["_workspace"] = ws
         return out
 
@@ -405,4 +423,5 @@ class Logprob:
         rlk_logprob_merge(self.handle, records.data_ptr(), targets.data_ptr(), T,
                           out["logp"].data_ptr(), out["lse"].data_ptr(), _ptr(out.get("entropy")),
                           _ptr(status), s.cuda_stream)
+        _on_stream(s, dev, *out.values())
         return out
