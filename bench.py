@@ -223,12 +223,20 @@ bf16_peak_at_sclk_tflops: {PEAK_BF16_TFLOPS * sclk / NOMINAL_SCLK_MHZ:.0f}
         f.write(text)
     print(text)
     stats = open(_one(os.path.join(base, "stats"), "kernel_stats.csv")).read()
-    n_lm = len(_durations(os.path.join(base, "stats"), "k_lmhead"))
+    dl = _durations(os.path.join(base, "stats"), "k_lmhead")
+    n_lm = len(dl)
+    warm = int(STATS_ARGS.split("--warmup")[1].split()[0])
+    timed = [dl[i] for i in sorted(dl)][warm:]  # dispatch order; the warm-up launches first
     head = f"""# Kernel durations, qwen3_8b_head workload (T=4096, H=4096, V=151936, one pass, 4 vocab segments)
 # command (from the repository root, TMPDIR=/tmp):
 #   {cmds["stats"]}
-# (run_kernel_stats.csv, durations in ns; {n_lm} LM-head calls = warmup + timed steps)
+# (run_kernel_stats.csv below, durations in ns; {n_lm} LM-head calls = {warm} warm-up + the
+# timed steps, which bench.py runs twice: without and with events around the kernel)
 # kernel_source_sha256: {kernel_source_sha()}
+lmhead_timed_launches: {len(timed)}
+lmhead_timed_mean_ms: {sum(timed) / len(timed) / 1e6:.4f}
+lmhead_timed_min_max_ms: {min(timed) / 1e6:.4f} {max(timed) / 1e6:.4f}
+lmhead_timed_frac_of_bf16_peak: {2 * 4096 * 4096 * 151936 / (sum(timed) / len(timed) * 1e-9) / 1e12 / PEAK_BF16_TFLOPS:.4f}
 """
     with open(PROFILE_STATS, "w") as f:
         f.write(head + stats)
@@ -255,10 +263,13 @@ def write_rollout_summary(base: str, cmds: dict, f_scale: float) -> None:
     mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
     rd = os.path.join(base, "rollout")
     stats = open(_one(rd, "kernel_stats.csv")).read()
-    dur = _durations(rd, "k_lmhead")
+    dur_all = _durations(rd, "k_lmhead")
     cf = _counters(os.path.join(base, "rfetch"), "k_lmhead")
     w_shard = (151936 // 4) * 4096 * 2
     per_step_launches = 120
+    warm = int(ROLLOUT_ARGS.split("--warmup")[1].split()[0])
+    # the timed launches: dispatch order, the warm-up steps' launches dropped
+    dur = {i: dur_all[i] for i in sorted(dur_all)[warm * per_step_launches:]}
     n = len(dur)
     tot_ms = sum(dur.values()) / 1e6
     fetch = [v * 1024 / f_scale for _, v in cf["FETCH_SIZE"]]
@@ -270,7 +281,7 @@ def write_rollout_summary(base: str, cmds: dict, f_scale: float) -> None:
 #   {cmds["rfetch"]}
 #   (FETCH_SIZE scaled by the 1 GiB copy of: {cmds["cfetch"]})
 # kernel_source_sha256: {kernel_source_sha()}
-lmhead_launches: {n} ({n // per_step_launches} steps incl. warmup)
+lmhead_launches_timed: {n} ({n // per_step_launches} timed steps; {warm} warm-up step(s) dropped)
 lmhead_mean_us_per_launch: {tot_ms * 1e3 / n:.1f}
 w_stream_GBps_from_trace: {n * w_shard / (tot_ms * 1e-3) / 1e9:.0f}
 w_stream_frac_of_8TBps: {n * w_shard / (tot_ms * 1e-3) / 8e12:.3f}
@@ -747,13 +758,19 @@ def main() -> int:
 
     ev = HipEvents(2 + 2 * args.steps)
     log(f"timing {args.steps} steps")
+    # the step as a caller runs it (no events inside): the throughput
     torch.cuda.synchronize()
     ev.record(0, sp)
-    for i in range(args.steps):
-        step((ev.ev[2 + 2 * i], ev.ev[3 + 2 * i]))
+    for _ in range(args.steps):
+        step()
     ev.record(1, sp)
     torch.cuda.synchronize()
     total_ms = ev.ms(0, 1)
+    # the same steps again with events around the LM-head launch: the kernel's own duration
+    log(f"timing {args.steps} steps with events around the LM-head kernel")
+    for i in range(args.steps):
+        step((ev.ev[2 + 2 * i], ev.ev[3 + 2 * i]))
+    torch.cuda.synchronize()
     k_ms = [ev.ms(2 + 2 * i, 3 + 2 * i) for i in range(args.steps)]
     ev.close()
     ms_step = total_ms / args.steps
