@@ -460,9 +460,14 @@ rlk_status_t forward_impl(rlk_logprob_t h, const void* hidden, const void* W_lm,
         ++launch_no;
       }
     }
-    const RowRange& br = p.batches[b];
-    const int64_t n = br.end - br.begin;
-    if (n == 0) continue;
+  }
+  // One fold over all rows of the call, after every batch's LM-head launches: the per-row
+  // arithmetic does not depend on which launch wrote a row's tile partials, so folding all of the
+  // call's batches at once gives each row the bits a fold per batch would (and 1 launch, not one
+  // per batch).
+  {
+    const RowRange br{0, T};
+    const int64_t n = T;
     rlk::FoldArgs f;
     f.part_m = reinterpret_cast<const float*>(ws + m.pm) + br.begin;
     f.part_s = reinterpret_cast<const float*>(ws + m.ps) + br.begin;
