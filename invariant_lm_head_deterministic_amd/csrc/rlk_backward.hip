@@ -40,6 +40,7 @@
 #include <utility>
 
 #include "rlk_device.h"
+#include "rlk_queue.h"
 
 namespace rlk {
 
@@ -70,42 +71,38 @@ struct GTile {
   int m0, mrows, n0, nrows;
 };
 
-// Block -> (A tile, B tile), XCD-aware as in the forward: consecutive block ids go round-robin to
-// the 8 XCDs, so they are remapped to let each XCD walk a contiguous range, a group of 8 A tiles
-// at a time across the B tiles. Returns false for the few padding blocks.
-__device__ __forceinline__ bool map_gemm(int M, int N, GTile& t) {
-  const int n_mt = (M + kGBM - 1) / kGBM, n_nt = (N + kGBN - 1) / kGBN;
-  const int64_t n_items = (int64_t)n_mt * n_nt;
-  const int64_t nblk = (n_items + 7) / 8 * 8;
-  const int64_t bid = blockIdx.x;
-  if (bid >= nblk) return false;
-  const int64_t L = (bid % 8) * (nblk / 8) + bid / 8;
-  if (L >= n_items) return false;
-  constexpr int GV = 8;
-  const int64_t grp = L / ((int64_t)GV * n_nt);
-  const int first = (int)(grp * GV);
-  const int gsz = min(GV, n_mt - first);
-  const int64_t within = L - grp * GV * n_nt;
-  const int mt = first + (int)(within % gsz);
-  const int nt = (int)(within / gsz);
-  t.m0 = uni(mt * kGBM);
-  t.mrows = uni(min(kGBM, M - mt * kGBM));
+// Item -> (A tile, batch, B tile). A launch's items are the A tiles x (batch, B tile) pairs,
+// handed out by per-XCD work queues (rlk_queue.h) in the forward's XCD-aware order: each XCD
+// walks a contiguous range of items, a group of 8 A tiles at a time across the B side.
+__device__ __forceinline__ void set_gtile(const GemmArgs& a, int vb, int tt, GTile& t, int& yb) {
+  const int y = tt / a.n_bt;
+  const int nt = tt - y * a.n_bt;
+  yb = uni(y);
+  t.m0 = uni(vb * kGBM);
+  t.mrows = uni(min(kGBM, a.M - vb * kGBM));
   t.n0 = uni(nt * kGBN);
-  t.nrows = uni(min(kGBN, N - nt * kGBN));
-  return true;
+  t.nrows = uni(min(kGBN, a.N - nt * kGBN));
 }
 
-int64_t gemm_blocks(int M, int N) {
-  const int64_t n = (int64_t)((M + kGBM - 1) / kGBM) * ((N + kGBN - 1) / kGBN);
-  return (n + 7) / 8 * 8;
+// Hands out one item of queue x (the count of items handed out from it before).
+__device__ __forceinline__ uint32_t gclaim(uint32_t* q, int x) {
+  return __hip_atomic_fetch_add(q + x, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Output row of this lane's B row in B block j of the wave (OUT epilogue), or null for a row past
-// the tile or a padding row of the segment-padded vocab layout. 32-bit index math: B rows are
-// below 2^31.
-__device__ __forceinline__ const float* out_row(const GemmArgs& a, const float* C, const GTile& t,
-                                                int wt, int j, int lane) {
-  const int nn = 16 * (wt * kGNB16 + j) + (lane & 15);
+// The item behind claim count c of queue (xq + qi) mod 8; a drained queue moves the block on to
+// the next queue, and false means that all eight are drained (at most eight claims).
+__device__ __forceinline__ bool gnext(const GemmArgs& a, int xq, int& qi, uint32_t c, int& vb,
+                                      int& tt) {
+  while (true) {
+    if (queue_item(a, (xq + qi) & (kQueues - 1), c, vb, tt)) return true;
+    if (++qi == kQueues) return false;
+    c = gclaim(a.queue, (xq + qi) & (kQueues - 1));
+  }
+}
+
+// Output row of tile B row nn (OUT epilogue), or null for a row past the tile or a padding row
+// of the segment-padded vocab layout. 32-bit index math: B rows are below 2^31.
+__device__ __forceinline__ float* out_row(const GemmArgs& a, float* C, const GTile& t, int nn) {
   if (nn >= t.nrows) return nullptr;
   const uint32_t n = (uint32_t)(t.n0 + nn);
   uint32_t row = n;
@@ -117,6 +114,17 @@ __device__ __forceinline__ const float* out_row(const GemmArgs& a, const float* 
     row = sg * L + c;
   }
   return C + (int64_t)row * a.ldc;
+}
+
+// Store shape of the epilogues. The MFMA result gives lane l = 16 g + r (r = l & 15) the row r of
+// a B block and 16 bytes of A block i at 16 i + 4 g; stored as is, one store instruction writes
+// 16 rows x 64 bytes (half cache lines), and a CU's store path takes about as long per line
+// touched as per full line (measured: 34 GB/s per CU against ~95 GB/s for 8 rows x 128 bytes).
+// So the data of two A blocks is regrouped across lanes first: with Y's rows rotated by 8 within
+// each 16 lanes (DPP row_ror:8), lanes r < 8 hold X of row r and Y of row r + 8, lanes r >= 8 the
+// reverse, and two store instructions write rows 0-7 and rows 8-15 as whole 128-byte lines.
+__device__ __forceinline__ uint32_t ror8(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xF, 0xF, false);
 }
 
 // One B1 value.
@@ -138,30 +146,18 @@ __device__ __forceinline__ uint16_t dz_one(float acc, int v, int y, float g, flo
   return (uint16_t)(bits & (0u - (uint32_t)(y >= 0)));
 }
 
-// The backward's NT GEMM tile kernel (see GemmArgs). EPI 0 = DZ, 1 = OUT.
-template <int EPI, bool ENTG, bool TEMP, bool PORT, bool ACC, bool ATR, bool BTR>
-__global__ void __launch_bounds__(64 * kGWaves) k_gemm(const GemmArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_a0[kGBM * kRowBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_a1[kGBM * kRowBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_b0[kGBN * kRowBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_b1[kGBN * kRowBytes];
-
-  GTile t;
-  if (!map_gemm(a.M, a.N, t)) return;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wv = wave % kGVW;
-  const int wt = wave / kGVW;
-  const int64_t yb = blockIdx.y;
+// Staging of one tile: per-lane DMA offsets of stage 0 and the operands' buffer descriptors.
+// Rows past the tile are clamped to its last row, as in the forward. DZ runs over the
+// segment-padded vocab positions: tile row m reads W row v(m), a padding position the last row
+// of its segment (its result is replaced by 0). v(m) never decreases, and the tile's real rows
+// are consecutive in W, so one descriptor from v(first) covers them.
+template <int EPI, bool ATR, bool BTR>
+__device__ __forceinline__ void gemm_stage(const GemmArgs& a, const GTile& t, int yb, int wave,
+                                           int lane, uint32_t (&ago)[kGWI],
+                                           uint32_t (&bgo)[kGHI], __amdgpu_buffer_rsrc_t& ra,
+                                           __amdgpu_buffer_rsrc_t& rb) {
   const uint16_t* __restrict__ Bt =
       BTR ? a.B + yb * a.b_batch + t.n0 : a.B + yb * a.b_batch + (int64_t)t.n0 * a.ldb;
-
-  // Staging offsets as in the forward: rows past the tile are clamped to its last row. DZ runs
-  // over the segment-padded vocab positions: tile row m reads W row v(m), a padding position
-  // the last row of its segment (its result is replaced by 0). v(m) never decreases, and the
-  // tile's real rows are consecutive in W, so one descriptor from v(first) covers them.
-  uint32_t ago[kGWI], bgo[kGHI];
   const uint16_t* __restrict__ At;
   int64_t a_rows;  // rows the A descriptor spans
   if constexpr (EPI == 0) {
@@ -224,101 +220,270 @@ __global__ void __launch_bounds__(64 * kGWaves) k_gemm(const GemmArgs a) {
       bgo[q] = (uint32_t)(((int64_t)min(r, t.nrows - 1) * a.ldb + c * 8) * 2);
     }
   }
-  const __amdgpu_buffer_rsrc_t ra =
-      ATR ? make_rsrc(At, tr_bytes(a.ka_rows, a.lda, t.m0))
-          : make_rsrc(At, (int)(((a_rows - 1) * a.lda + a.K) * 2));
-  const __amdgpu_buffer_rsrc_t rb =
-      BTR ? make_rsrc(Bt, tr_bytes(a.kb_rows, a.ldb, t.n0))
-          : make_rsrc(Bt, (int)(((int64_t)(t.nrows - 1) * a.ldb + a.K) * 2));
+  ra = ATR ? make_rsrc(At, tr_bytes(a.ka_rows, a.lda, t.m0))
+           : make_rsrc(At, (int)(((a_rows - 1) * a.lda + a.K) * 2));
+  rb = BTR ? make_rsrc(Bt, tr_bytes(a.kb_rows, a.ldb, t.n0))
+           : make_rsrc(Bt, (int)(((int64_t)(t.nrows - 1) * a.ldb + a.K) * 2));
+}
 
-  float* __restrict__ C = EPI == 1 ? a.C + yb * a.c_batch : nullptr;
-  f32x4 acc[kGVB16][kGNB16];
+// DMA of K stage kc of both operands into (la, lb), as the K loop issues it; sa / sb: bytes
+// from one K stage to the next of a K-major operand.
+template <bool ATR, bool BTR>
+__device__ __forceinline__ void gemm_issue(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                           const uint32_t (&ago)[kGWI],
+                                           const uint32_t (&bgo)[kGHI], int kc, uint8_t* la,
+                                           uint8_t* lb, int wave, uint32_t sa, uint32_t sb) {
+  const uint32_t so = (uint32_t)kc * kRowBytes;
+  const uint32_t soa = ATR ? (uint32_t)kc * sa : so;
+  const uint32_t sob = BTR ? (uint32_t)kc * sb : so;
 #pragma unroll
-  for (int i = 0; i < kGVB16; ++i)
+  for (int q = 0; q < kGWI; ++q) dma16(ra, la + 8 * (q * kGWaves + wave) * kRowBytes, ago[q], soa);
 #pragma unroll
-    for (int j = 0; j < kGNB16; ++j)
+  for (int q = 0; q < kGHI; ++q) dma16(rb, lb + 8 * (q * kGWaves + wave) * kRowBytes, bgo[q], sob);
+}
+
+// The B1 inputs of this lane's rows (lane & 15 of each of the wave's B blocks).
+struct DzRows {
+  int y[kGNB16];
+  float g[kGNB16], l[kGNB16], h[kGNB16], e[kGNB16];
+};
+
+template <bool ENTG>
+__device__ __forceinline__ void dz_rows(const GemmArgs& a, const GTile& t, int wt, int ln,
+                                        DzRows& r) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0f;
-  if constexpr (EPI == 1 && ACC) {
-    static_for<kGNB16>([&](auto jc) {
-      constexpr int j = decltype(jc)::value;
-      const float* crow = out_row(a, C, t, wt, j, lane);
-      if (!crow) return;
-      const int mb = t.m0 + 16 * wv * kGVB16 + 4 * (lane >> 4);
-      static_for<kGVB16>([&](auto ic) {
-        constexpr int i = decltype(ic)::value;
-        if (mb + 16 * i < a.M) acc[i][j] = *(const f32x4*)(crow + mb + 16 * i);
-      });
-    });
+  for (int j = 0; j < kGNB16; ++j) {
+    const int nn = 16 * (wt * kGNB16 + j) + (ln & 15);
+    const bool ok = nn < t.nrows;
+    const int64_t n = t.n0 + (ok ? nn : 0);
+    r.y[j] = ok ? a.targets[n] : -1;
+    r.g[j] = a.g[n];
+    r.l[j] = a.lse[n];
+    r.h[j] = ENTG ? a.gH[n] : 0.0f;
+    r.e[j] = ENTG ? a.ent[n] : 0.0f;
   }
-  nt_mainloop<kGWaves, kGVB16, kGNB16, kGWI, kGHI, ATR, BTR>(
-      acc, lds_a0, lds_a1, lds_b0, lds_b1, ra, rb, ago, bgo, a.K / kKStage, wave, lane, wv, wt,
-      (uint32_t)(64 * a.lda * 2), (uint32_t)(64 * a.ldb * 2));
+}
 
-  // The epilogues index the accumulators with compile-time constants (static_for): a runtime
-  // index would move them to scratch. The lane id goes through an empty asm so that the compiler
-  // recomputes every address from it instead of keeping the prologue's alive across the K loop.
-  int ln = lane;
-  __asm__ volatile("" : "+v"(ln));
-  if constexpr (EPI == 1) {
-    // one output row pointer per B block (row(n) needs one division), then constant offsets
-    static_for<kGNB16>([&](auto jc) {
-      constexpr int j = decltype(jc)::value;
-      float* crow = const_cast<float*>(out_row(a, C, t, wt, j, ln));
-      if (!crow) return;
-      const int mb = t.m0 + 16 * wv * kGVB16 + 4 * (ln >> 4);
-      static_for<kGVB16>([&](auto ic) {
-        constexpr int i = decltype(ic)::value;
-        if (mb + 16 * i < a.M) *(f32x4*)(crow + mb + 16 * i) = acc[i][j];
-      });
-    });
-  } else {
-    // B1 on the result registers: lane holds rows n = token (lane & 15 of each B block) and
-    // 4 consecutive vocab indices m per A block
-    int yj[kGNB16];
-    float gj[kGNB16], lj[kGNB16], hj[kGNB16], ej[kGNB16];
-#pragma unroll
-    for (int j = 0; j < kGNB16; ++j) {
-      const int nn = 16 * (wt * kGNB16 + j) + (ln & 15);
-      const bool ok = nn < t.nrows;
-      const int64_t n = t.n0 + (ok ? nn : 0);
-      yj[j] = ok ? a.targets[n] : -1;
-      gj[j] = a.g[n];
-      lj[j] = a.lse[n];
-      hj[j] = ENTG ? a.gH[n] : 0.0f;
-      ej[j] = ENTG ? a.ent[n] : 0.0f;
-    }
-    // hoisted addressing: the lane's dz row for B block 0 (block j adds 16 rows); positions,
-    // segments and vocab indices in 32-bit math (< 2^31)
-    const int64_t tl = t.n0 + 16 * wt * kGNB16 + (ln & 15);
-    uint16_t* const dzr = a.dz + tl * a.lddz;
-    const int64_t dz_j = 16 * a.lddz;
-    const uint32_t L = (uint32_t)a.seg_len, Lp = (uint32_t)a.seg_pad;
-    const uint32_t cb = (uint32_t)(t.m0 + 16 * wv * kGVB16 + 4 * (ln >> 4));
-    static_for<kGVB16>([&](auto ic) {
-      constexpr int i = decltype(ic)::value;
-      // 4 consecutive padded positions col0 .. col0+3 (one segment: Lp is a multiple of 128)
-      const uint32_t col0 = cb + 16 * i;
-      const uint32_t sg = col0 / Lp;
-      const uint32_t c0 = col0 - sg * Lp;  // position inside the segment
-      const int v0 = (int)(a.v_base + sg * L + c0);  // vocab index of col0 when c0 < L
-      const bool col_ok = (int)col0 < a.M;
-      static_for<kGNB16>([&](auto jc) {
-        constexpr int j = decltype(jc)::value;
-        const int nn = 16 * (wt * kGNB16 + j) + (ln & 15);
-        if (nn >= t.nrows || !col_ok) return;
+// B1 on the result registers: lane l holds the token row l & 15 of each B block and 4
+// consecutive vocab positions of each A block, which become 4 bf16 (8 bytes). A group of four A
+// blocks (64 positions = 128 bytes of a dz row) is regrouped to 16 bytes per lane in two steps:
+// v_permlane16_swap exchanges 16-lane rows 1 <-> 0 and 3 <-> 2 between blocks (i, i+1), so that
+// lane 16 g + r holds positions 8 (g >> 1) .. +7 of block i + (g & 1) (likewise P for blocks
+// i+2, i+3), then the ror8 step above pairs token rows r and r + 8. The epilogues index the
+// accumulators with compile-time constants (static_for): a runtime index would move them to
+// scratch.
+template <bool ENTG, bool TEMP, bool PORT>
+__device__ __forceinline__ void dz_epilogue(const GemmArgs& a, f32x4 (&acc)[kGVB16][kGNB16],
+                                            const DzRows& rw, const GTile& t, int wv, int wt,
+                                            int ln) {
+  const int r = ln & 15, g = ln >> 4;
+  const bool lo = r < 8;
+  const uint32_t L = (uint32_t)a.seg_len, Lp = (uint32_t)a.seg_pad;
+  const uint32_t wb = (uint32_t)(t.m0 + 16 * wv * kGVB16);  // the wave's first position
+  const uint32_t cb = wb + 4 * g;                            // this lane's position in block 0
+  // position of this lane's 16 bytes after the regrouping, in the group's first block pair
+  const uint32_t cp = wb + 16 * (g & 1) + 8 * (g >> 1);
+  static_for<kGNB16>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    const int nn_a = 16 * (wt * kGNB16 + j) + (r & 7);  // rows of the two stores
+    const bool ok_a = nn_a < t.nrows, ok_b = nn_a + 8 < t.nrows;
+    uint16_t* const da = a.dz + (t.n0 + (int64_t)nn_a) * a.lddz;
+    uint16_t* const db = da + 8 * a.lddz;
+    static_for<kGVB16 / 4>([&](auto gc) {
+      constexpr int i0 = 4 * decltype(gc)::value;
+      uint32_t w[4][2];  // the lane's 4 bf16 of blocks i0 .. i0+3
+      static_for<4>([&](auto qc) {
+        constexpr int q = decltype(qc)::value;
+        const uint32_t col0 = cb + 16 * (i0 + q);
+        const uint32_t sg = col0 / Lp;
+        const uint32_t c0 = col0 - sg * Lp;           // position inside the segment
+        const int v0 = (int)(a.v_base + sg * L + c0);  // vocab index of col0 when c0 < L
         uint16_t b[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const uint16_t x = dz_one<ENTG, TEMP, PORT>(acc[i][j][r], v0 + r, yj[j], gj[j], lj[j],
-                                                      hj[j], ej[j], a.inv_tau);
-          b[r] = c0 + r < L ? x : (uint16_t)0;
+        for (int e = 0; e < 4; ++e) {
+          const uint16_t x = dz_one<ENTG, TEMP, PORT>(acc[i0 + q][j][e], v0 + e, rw.y[j],
+                                                      rw.g[j], rw.l[j], rw.h[j], rw.e[j],
+                                                      a.inv_tau);
+          b[e] = c0 + e < L ? x : (uint16_t)0;
         }
-        const uint32_t w0 = (uint32_t)b[0] | ((uint32_t)b[1] << 16);
-        const uint32_t w1 = (uint32_t)b[2] | ((uint32_t)b[3] << 16);
-        *(uint2*)(dzr + j * dz_j + col0) = make_uint2(w0, w1);
+        w[q][0] = (uint32_t)b[0] | ((uint32_t)b[1] << 16);
+        w[q][1] = (uint32_t)b[2] | ((uint32_t)b[3] << 16);
       });
+      uint32_t P[4], Q[4];
+      {
+        const auto s0 = __builtin_amdgcn_permlane16_swap(w[0][0], w[1][0], false, false);
+        const auto s1 = __builtin_amdgcn_permlane16_swap(w[0][1], w[1][1], false, false);
+        const auto s2 = __builtin_amdgcn_permlane16_swap(w[2][0], w[3][0], false, false);
+        const auto s3 = __builtin_amdgcn_permlane16_swap(w[2][1], w[3][1], false, false);
+        P[0] = s0[0]; P[1] = s1[0]; P[2] = s0[1]; P[3] = s1[1];
+        Q[0] = s2[0]; Q[1] = s3[0]; Q[2] = s2[1]; Q[3] = s3[1];
+      }
+      u32x4 pv, zv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pv[e] = P[e];
+        zv[e] = ror8(Q[e]);
+      }
+      const uint32_t c_p = cp + 16 * i0;  // P's positions; Q's are 32 further
+      const uint32_t ca = lo ? c_p : c_p + 32, cbb = lo ? c_p + 32 : c_p;
+      if (ok_a && (int)ca < a.M) *(u32x4*)(da + ca) = lo ? pv : zv;
+      if (ok_b && (int)cbb < a.M) *(u32x4*)(db + cbb) = lo ? zv : pv;
     });
+  });
+}
+
+// OUT: fp32, A blocks (i, i+1) regrouped as above into two stores of 8 rows x 128 bytes.
+__device__ __forceinline__ void out_store(const GemmArgs& a, f32x4 (&acc)[kGVB16][kGNB16],
+                                          const GTile& t, int yb, int wv, int wt, int ln) {
+  float* C = a.C + yb * a.c_batch;
+  const int r = ln & 15, g = ln >> 4;
+  const bool lo = r < 8;
+  const int mb = t.m0 + 16 * wv * kGVB16 + 4 * g;  // this lane's column in A block 0
+  static_for<kGNB16>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    const int nn_a = 16 * (wt * kGNB16 + j) + (r & 7);
+    float* const ra = out_row(a, C, t, nn_a);
+    float* const rb = out_row(a, C, t, nn_a + 8);
+    static_for<kGVB16 / 2>([&](auto pc) {
+      constexpr int i0 = 2 * decltype(pc)::value;
+      const f32x4 X = acc[i0][j];
+      f32x4 Z;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Z[e] = __uint_as_float(ror8(__float_as_uint(acc[i0 + 1][j][e])));
+      const int c = mb + 16 * i0;  // X's columns; Z's are 16 further
+      const int ca = lo ? c : c + 16, cbb = lo ? c + 16 : c;
+      if (ra && ca < a.M) *(f32x4*)(ra + ca) = lo ? X : Z;
+      if (rb && cbb < a.M) *(f32x4*)(rb + cbb) = lo ? Z : X;
+    });
+  });
+}
+
+// ACC: the stored values as the chain's start, in the MFMA result layout.
+__device__ __forceinline__ void out_load(const GemmArgs& a, f32x4 (&acc)[kGVB16][kGNB16],
+                                         const GTile& t, int yb, int wv, int wt, int ln) {
+  float* C = a.C + yb * a.c_batch;
+  static_for<kGNB16>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    const float* crow = out_row(a, C, t, 16 * (wt * kGNB16 + j) + (ln & 15));
+    if (!crow) return;
+    const int mb = t.m0 + 16 * wv * kGVB16 + 4 * (ln >> 4);
+    static_for<kGVB16>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if (mb + 16 * i < a.M) acc[i][j] = *(const f32x4*)(crow + mb + 16 * i);
+    });
+  });
+}
+
+// The backward's NT GEMM kernel (see GemmArgs). EPI 0 = DZ, 1 = OUT.
+// Persistent, as the forward's LM-head kernel: one block per CU takes items from its XCD's work
+// queue, then from the other XCDs' queues. Once every wave is past an item's last fragment read,
+// the first two K stages of the next item are issued, and only then does the item's epilogue
+// compute and store its results, so the next item's loads overlap them. Which block computes an
+// item never changes its arithmetic, so the bits do not depend on the schedule.
+template <int EPI, bool ENTG, bool TEMP, bool PORT, bool ACC, bool ATR, bool BTR>
+__global__ void __launch_bounds__(64 * kGWaves) k_gemm(const GemmArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_a0[kGBM * kRowBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_a1[kGBM * kRowBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_b0[kGBN * kRowBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_b1[kGBN * kRowBytes];
+  // the block's next item (A tile, batch x B tile), -1 when every queue is drained, and the
+  // queue offset of its claims; written by thread 0, read after barriers
+  __shared__ int s_next[2];
+  __shared__ int s_qi;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wv = wave % kGVW;
+  const int wt = wave / kGVW;
+  const bool leader = tid == 0;
+  const int nk = a.K / kKStage;
+  const uint32_t sa = (uint32_t)(64 * a.lda * 2), sb = (uint32_t)(64 * a.ldb * 2);
+  // this XCD's queue: the XCC_ID hardware register (the id is bits 3:0)
+  auto xcc_queue = []() { return (int)(__builtin_amdgcn_s_getreg((31 << 11) | 20) & (kQueues - 1)); };
+  // The arguments again from the kernel-argument segment, by scalar loads through a pointer the
+  // compiler cannot see through: what the item boundary needs is loaded there instead of held in
+  // scalar registers across the K loop.
+  typedef const __attribute__((address_space(4))) GemmArgs* kargs_t;
+  auto args = []() -> const GemmArgs& {
+    uint64_t p = (uint64_t)__builtin_amdgcn_kernarg_segment_ptr();
+    __asm__ volatile("" : "+s"(p));
+    return *(const GemmArgs*)(kargs_t)p;
+  };
+  uint32_t pend = 0;  // thread 0: claim count in flight for the next item
+
+  if (leader) {
+    const int xq = xcc_queue();
+    int qi = 0, vb = -1, tt = 0;
+    if (!gnext(a, xq, qi, gclaim(a.queue, xq), vb, tt)) vb = -1;
+    s_next[0] = vb;
+    s_next[1] = tt;
+    s_qi = qi;
+  }
+  __syncthreads();
+  if (uni(s_next[0]) >= 0) {
+    GTile t;
+    int yb;
+    set_gtile(a, uni(s_next[0]), uni(s_next[1]), t, yb);
+    uint32_t ago[kGWI], bgo[kGHI];
+    __amdgpu_buffer_rsrc_t ra, rb;
+    gemm_stage<EPI, ATR, BTR>(a, t, yb, wave, lane, ago, bgo, ra, rb);
+    gemm_issue<ATR, BTR>(ra, rb, ago, bgo, 0, lds_a0, lds_b0, wave, sa, sb);
+    gemm_issue<ATR, BTR>(ra, rb, ago, bgo, 1, lds_a1, lds_b1, wave, sa, sb);
+    if (leader) pend = gclaim(a.queue, (xcc_queue() + s_qi) & (kQueues - 1));
+    while (true) {
+      f32x4 acc[kGVB16][kGNB16];
+#pragma unroll
+      for (int i = 0; i < kGVB16; ++i)
+#pragma unroll
+        for (int j = 0; j < kGNB16; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0f;
+      if constexpr (EPI == 1 && ACC) out_load(args(), acc, t, yb, wv, wt, lane);
+      auto resolve = [&]() {
+        if (leader) {
+          int qi = s_qi, nv = -1, nt = 0;
+          if (!gnext(args(), xcc_queue(), qi, pend, nv, nt)) nv = -1;
+          s_next[0] = nv;
+          s_next[1] = nt;
+          s_qi = qi;
+        }
+      };
+      nt_mainloop_x<kGWaves, kGVB16, kGNB16, kGWI, kGHI, ATR, BTR, true>(
+          acc, lds_a0, lds_a1, lds_b0, lds_b1, ra, rb, ago, bgo, nk, wave, lane, wv, wt, sa, sb,
+          resolve);
+      __syncthreads();
+      const GemmArgs& b = args();
+      // an opaque copy of the lane id: what the epilogue derives from it is computed here, not
+      // hoisted out of the item loop and held across the K loop
+      int ln = lane;
+      __asm__ volatile("" : "+v"(ln));
+      // B1's row inputs are loaded before the next item's DMAs, so that waiting for them does
+      // not wait for those
+      DzRows rw;
+      if constexpr (EPI == 0) dz_rows<ENTG>(b, t, wt, ln, rw);
+      const int nv = uni(s_next[0]);
+      if (nv >= 0) {
+        GTile tn;
+        int yn;
+        set_gtile(b, nv, uni(s_next[1]), tn, yn);
+        gemm_stage<EPI, ATR, BTR>(b, tn, yn, wave, ln, ago, bgo, ra, rb);
+        gemm_issue<ATR, BTR>(ra, rb, ago, bgo, 0, lds_a0, lds_b0, wave, sa, sb);
+        gemm_issue<ATR, BTR>(ra, rb, ago, bgo, 1, lds_a1, lds_b1, wave, sa, sb);
+        if (leader) pend = gclaim(b.queue, (xcc_queue() + s_qi) & (kQueues - 1));
+      }
+      if constexpr (EPI == 1) out_store(b, acc, t, yb, wv, wt, ln);
+      else dz_epilogue<ENTG, TEMP, PORT>(b, acc, rw, t, wv, wt, ln);
+      if (nv < 0) break;
+      // the next item again from the queue's answer, rather than held across the epilogue
+      __asm__ volatile("" ::: "memory");
+      set_gtile(args(), uni(s_next[0]), uni(s_next[1]), t, yb);
+    }
+  }
+  // the last block of the launch to get here resets the queues for the next launch
+  if (leader && gclaim(a.queue, kQueues) == gridDim.x - 1) {
+    for (int x = 0; x <= kQueues; ++x)
+      __hip_atomic_exchange(a.queue + x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -466,30 +631,51 @@ hipError_t launch_dgamma(const float* dy, const uint16_t* x, const float* r, flo
   return hipGetLastError();
 }
 
+// Persistent launch over batches x the A tiles x B tiles of one GEMM: one block per CU (the
+// kernel's LDS allows no second), fewer when there are fewer items; the queues must be zero, and
+// the kernel leaves them zero.
+static bool gemm_grid(GemmArgs& q, int batches, dim3& grid) {
+  const int64_t n_mt = (q.M + kGBM - 1) / kGBM, n_nt = (q.N + kGBN - 1) / kGBN;
+  const int64_t n_tt = n_nt * batches;
+  const int64_t items = n_mt * n_tt;
+  if (items > 0x7fffffffLL - 8 * 4096) return false;
+  q.n_bt = (int32_t)n_nt;
+  // one band per batch: every XCD works through the batches in order, so that at any time the
+  // whole device streams the same batch's A operand (one vocab segment of W for dh), as a plain
+  // launch of one grid slice per batch would
+  queue_setup(q, n_mt, n_tt, n_nt);
+  grid = dim3((unsigned)std::min<int64_t>(items, q.n_cu > 0 ? q.n_cu : 256));
+  return true;
+}
+
 hipError_t launch_gemm_dz(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
-  const int64_t blocks = gemm_blocks(a.M, a.N);
-  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (!a.queue) return hipErrorInvalidValue;
+  GemmArgs q = a;
+  dim3 grid;
+  if (!gemm_grid(q, 1, grid)) return hipErrorInvalidConfiguration;
   with_bwd_modes(a.gH != nullptr, a.inv_tau != 1.0f, a.portable != 0,
                  [&](auto e, auto t, auto p) {
                    hipLaunchKernelGGL((k_gemm<0, e.value, t.value, p.value, false, false, false>),
-                                      dim3((unsigned)blocks), dim3(64 * kGWaves), 0, s, a);
+                                      grid, dim3(64 * kGWaves), 0, s, q);
                  });
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_out(const GemmArgs& a, int batches, bool b_trans, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0 || batches <= 0) return hipSuccess;
-  const int64_t blocks = gemm_blocks(a.M, a.N);
-  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  const dim3 grid((unsigned)blocks, (unsigned)batches), block(64 * kGWaves);
+  if (!a.queue) return hipErrorInvalidValue;
+  GemmArgs q = a;
+  dim3 grid;
+  if (!gemm_grid(q, batches, grid)) return hipErrorInvalidConfiguration;
+  const dim3 block(64 * kGWaves);
   // dh: A (W) K-major, B (dz) K-contiguous; dW: both K-major (hidden rows, dz)
   if (b_trans) {
-    if (a.accumulate) hipLaunchKernelGGL((k_gemm<1, false, false, false, true, true, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_gemm<1, false, false, false, false, true, true>), grid, block, 0, s, a);
+    if (a.accumulate) hipLaunchKernelGGL((k_gemm<1, false, false, false, true, true, true>), grid, block, 0, s, q);
+    else hipLaunchKernelGGL((k_gemm<1, false, false, false, false, true, true>), grid, block, 0, s, q);
   } else {
-    if (a.accumulate) hipLaunchKernelGGL((k_gemm<1, false, false, false, true, true, false>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_gemm<1, false, false, false, false, true, false>), grid, block, 0, s, a);
+    if (a.accumulate) hipLaunchKernelGGL((k_gemm<1, false, false, false, true, true, false>), grid, block, 0, s, q);
+    else hipLaunchKernelGGL((k_gemm<1, false, false, false, false, true, false>), grid, block, 0, s, q);
   }
   return hipGetLastError();
 }

@@ -690,7 +690,7 @@ namespace {
 struct BwdMap {
   int64_t L, Lp, J;    // segment length, padded length, padded vocab width S_c Lp
   int64_t chunk;       // rows per chunk
-  size_t dz, dpart, y, dy, r, gp, total;
+  size_t status, dz, dpart, y, dy, r, gp, total;
 };
 
 // Rows per chunk: the caller's row_chunk (or all rows), capped so that the dz rows of a chunk
@@ -722,6 +722,7 @@ BwdMap bwd_map(const rlk_logprob_config_t& c, int64_t rows, int64_t row_chunk, b
     off = round_up(off + bytes, 256);
     return at;
   };
+  m.status = take(rlk::kStatusSlotWords * 4);  // the GEMMs' work queues (from word kQueueWord)
   m.dz = take((size_t)m.chunk * (size_t)m.J * 2);
   m.dpart = (want_h && S > 1 && !shard) ? take((size_t)S * (size_t)m.chunk * H * 4) : 0;
   const bool rms = c.flags & RLK_FLAG_RMSNORM;
@@ -811,6 +812,10 @@ rlk_status_t backward_run(const rlk_logprob* h, const BwdRun& b, void* workspace
   const uint16_t* gam = b.gamma;
   const uint16_t* hid = b.hidden;
   const uint16_t* Wb = b.W;
+  // the persistent GEMMs' work queues: zero before the first, and each launch leaves them zero
+  uint32_t* queue = reinterpret_cast<uint32_t*>(ws + m.status) + rlk::kQueueWord;
+  e = rlk::launch_clear_status(reinterpret_cast<uint32_t*>(ws + m.status), nullptr, 0, s);
+  if (e != hipSuccess) return hip_fail(e, "clear launch");
   int64_t chunk_no = 0;
   for (int64_t r0 = 0; r0 < num_rows; r0 += m.chunk, ++chunk_no) {
     const int64_t r1 = std::min<int64_t>(num_rows, r0 + m.chunk);
@@ -853,6 +858,8 @@ rlk_status_t backward_run(const rlk_logprob* h, const BwdRun& b, void* workspace
     a.v_base = (int64_t)b.s0 * m.L;
     a.inv_tau = c.inv_temperature;
     a.portable = (c.flags & RLK_FLAG_PORTABLE_EXP) ? 1 : 0;
+    a.queue = queue;
+    a.n_cu = h->n_cu;
     e = rlk::launch_gemm_dz(a, s);
     if (e != hipSuccess) return hip_fail(e, "dz launch");
     if (want_h) {
@@ -879,6 +886,8 @@ rlk_status_t backward_run(const rlk_logprob* h, const BwdRun& b, void* workspace
         g.c_batch = n * H;
       }
       g.ldc = H;
+      g.queue = queue;
+      g.n_cu = h->n_cu;
       e = rlk::launch_gemm_out(g, S, false, s);
       if (e != hipSuccess) return hip_fail(e, "dh launch");
       if (S > 1 && !shard) {
@@ -926,6 +935,8 @@ rlk_status_t backward_run(const rlk_logprob* h, const BwdRun& b, void* workspace
       g.ldc = H;
       g.accumulate = (accumulate || chunk_no > 0) ? 1 : 0;
       g.map_rows = 1;
+      g.queue = queue;
+      g.n_cu = h->n_cu;
       e = rlk::launch_gemm_out(g, 1, true, s);
       if (e != hipSuccess) return hip_fail(e, "dW launch");
     }

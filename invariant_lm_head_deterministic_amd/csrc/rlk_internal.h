@@ -146,6 +146,12 @@ struct GemmArgs {
   int64_t v_base;           // global vocab index of position 0 (a shard's first row)
   float inv_tau;
   int32_t portable;
+  // persistent launch: work queues ([kQueueWords] counters, zero at launch, left zero) and the
+  // item geometry (queue_setup over the A tiles x (batch, B tile) pairs)
+  uint32_t* queue;
+  int32_t n_cu;
+  int32_t n_bt;             // B tiles per batch
+  int32_t q_nvb, q_rb, q_nfull, q_perf, q_tail_tt, q_pert;
 };
 
 

@@ -1,7 +1,8 @@
-// Work queues of the persistent LM-head kernel (k_lmhead). Host and device code: the launcher
-// sets a launch's item geometry with queue_setup, every block maps the claims it makes to items
-// with queue_item, and a host program enumerates every queue to check that the items of a launch
-// are handed out exactly once.
+// Work queues of the persistent kernels (the LM-head kernel k_lmhead and the backward GEMMs).
+// Host and device code: the launcher sets a launch's item geometry with queue_setup, every block
+// maps the claims it makes to items with queue_item, and a host program enumerates every queue to
+// check that the items of a launch are handed out exactly once. Q is the launch's argument struct
+// (LmheadArgs or GemmArgs), which carries the geometry in its q_* fields.
 //
 // A launch's items are its (vocab block, row tile) pairs. Row tiles go in bands (the hidden rows
 // of a band stay in the MALL while the vocabulary streams past them), one band after the other.
@@ -25,8 +26,8 @@ __host__ __device__ inline int qmin(int a, int b) { return a < b ? a : b; }
 __host__ __device__ inline int qmax(int a, int b) { return a > b ? a : b; }
 
 // Item geometry of a launch of n_vb vocab blocks x n_tt row tiles in bands of rb row tiles.
-__host__ __device__ inline void queue_setup(LmheadArgs& q, int64_t n_vb, int64_t n_tt,
-                                            int64_t rb) {
+template <class Q>
+__host__ __device__ inline void queue_setup(Q& q, int64_t n_vb, int64_t n_tt, int64_t rb) {
   q.q_nvb = (int32_t)n_vb;
   q.q_rb = (int32_t)(rb < n_tt ? rb : n_tt);
   q.q_nfull = (int32_t)(n_tt / q.q_rb);
@@ -36,8 +37,8 @@ __host__ __device__ inline void queue_setup(LmheadArgs& q, int64_t n_vb, int64_t
 }
 
 // The c-th item of queue x in (vb, tt); false past the queue's end.
-__host__ __device__ inline bool queue_item(const LmheadArgs& a, int x, uint32_t c, int& vb,
-                                           int& tt) {
+template <class Q>
+__host__ __device__ inline bool queue_item(const Q& a, int x, uint32_t c, int& vb, int& tt) {
   const int nvb = a.q_nvb;
   const int len_f = qmax(0, qmin(a.q_perf, nvb * a.q_rb - x * a.q_perf));  // per full band
   const uint32_t c_full = (uint32_t)(a.q_nfull * len_f);
