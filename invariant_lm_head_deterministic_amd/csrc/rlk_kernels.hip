@@ -443,9 +443,11 @@ k_lmhead(const LmheadArgs a) {
 // are outstanding while one is read.
 // HS > 0: W streams through its own ring of NS stages and the hidden rows through a ring of HS
 // (they are L2-resident and arrive quickly), so the same LDS holds more W in flight. Measured
-// per vocab segment: 193-256 rows 106 -> 92 us (3 + 2 stages), 65-128 rows 74 -> 73 us
-// (4 + 3); no gain for 129-192 rows, and slower at <= 64 rows with a ring of 2 for the hidden
-// rows, whose short stages leave those too little time.
+// per vocab segment: 193-256 rows 106 -> 92 us (3 + 2 stages), 65-128 rows with 6 waves
+// 74 -> 73 us (4 + 3); slower at <= 64 rows with a ring of 2 for the hidden rows, whose short
+// stages leave those too little time, and for 65-192 rows with 12 waves (one ring of 3 stages:
+// 70-80 us; 4 + 2 stages: 77-84 us).
+// NB16 (token blocks of 16 per wave) may be odd: 12 waves of 48 rows cover 192.
 // The stage buffer is picked at run time; the DMA is issued from inline assembly so that the
 // compiler, which cannot tell the stage buffers apart at run time, does not wait for every
 // outstanding DMA before each LDS read. Its completion is awaited explicitly (vmcnt) before the
@@ -480,13 +482,13 @@ __device__ __forceinline__ void wait_vm() {
   __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(D) : "memory");
 }
 
-template <int VW, int TW, int NTB, int NS, int NTPB, int HS, bool ENT, bool TEMP, bool PORT>
+template <int VW, int TW, int NB16, int NS, int NTPB, int HS, bool ENT, bool TEMP, bool PORT>
 __global__ void __launch_bounds__(64 * VW * TW) k_lmhead_deep(const LmheadArgs a) {
+  // NB16: token blocks of 16 per wave
   constexpr int NWAVES = VW * TW;
-  constexpr int BT = 32 * NTB * TW;
+  constexpr int BT = 16 * NB16 * TW;
   constexpr int BW = NTPB * kVocabTile;  // block columns
   constexpr int VB16 = BW / 16 / VW;     // vocab blocks of 16 per wave
-  constexpr int NB16 = 2 * NTB;          // token blocks of 16 per wave
   constexpr int WI = BW / 8 / NWAVES;
   // hidden rows are staged in whole DMA rounds of 8 NWAVES rows; rows past BT repeat the last
   // row and are never read
@@ -1165,15 +1167,15 @@ static hipError_t launch_stream(const LmheadArgs& a, bool ent, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int VW, int TW, int NTB, int NS, int NTPB, int HS = 0>
+template <int VW, int TW, int NB16, int NS, int NTPB, int HS = 0>
 static hipError_t launch_deep(const LmheadArgs& a, bool ent, hipStream_t s) {
-  constexpr int BT = 32 * NTB * TW;
+  constexpr int BT = 16 * NB16 * TW;
   const int64_t blocks = lmhead_blocks<BT, NTPB>(a);
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)blocks), block(64 * VW * TW);
   with_modes(a, ent, [&](auto e, auto t, auto p) {
-    hipLaunchKernelGGL((k_lmhead_deep<VW, TW, NTB, NS, NTPB, HS, e.value, t.value, p.value>), grid,
+    hipLaunchKernelGGL((k_lmhead_deep<VW, TW, NB16, NS, NTPB, HS, e.value, t.value, p.value>), grid,
                        block, 0, s, a);
   });
   return hipGetLastError();
@@ -1206,18 +1208,20 @@ hipError_t launch_lmhead(const LmheadArgs& a, int bt, bool ent, hipStream_t s) {
       return launch_stream<2, 1, 3, 128, 8, 2>(a, ent, s);
     }
     if (three_tile_blocks(a)) {
-      if (a.rows > 192) return launch_deep<3, 4, 2, 3, 3, 2>(a, ent, s);
-      if (a.rows > 128) return launch_deep<3, 2, 3, 3, 3>(a, ent, s);
-      if (a.rows > 64) return launch_deep<3, 2, 2, 4, 3, 3>(a, ent, s);
-      return launch_deep<3, 2, 1, 3, 3>(a, ent, s);
+      if (a.rows > 192) return launch_deep<3, 4, 4, 3, 3, 2>(a, ent, s);
+      // 12 waves (3 per SIMD; 6 waves would load two SIMDs with two waves and two with one):
+      // 48 or 32 rows per wave, W and the hidden rows in one ring of 3 stages
+      if (a.rows > 128) return launch_deep<3, 4, 3, 3, 3>(a, ent, s);
+      if (a.rows > 64) return launch_deep<3, 4, 2, 3, 3>(a, ent, s);
+      return launch_deep<3, 2, 2, 3, 3>(a, ent, s);
     }
     bt = a.rows > 128 ? 256 : a.rows > 64 ? 128 : a.rows > 32 ? 64 : 32;
   }
   switch (bt) {
     case 256: return launch_variant<2, 4, 2>(a, ent, s);
-    case 128: return launch_deep<2, 2, 2, 3, 4>(a, ent, s);
-    case 64: return launch_deep<4, 1, 2, 3, 4>(a, ent, s);
-    case 32: return launch_deep<4, 1, 1, 4, 4>(a, ent, s);
+    case 128: return launch_deep<2, 2, 4, 3, 4>(a, ent, s);
+    case 64: return launch_deep<4, 1, 4, 3, 4>(a, ent, s);
+    case 32: return launch_deep<4, 1, 2, 4, 4>(a, ent, s);
     default: return hipErrorInvalidValue;
   }
 }
