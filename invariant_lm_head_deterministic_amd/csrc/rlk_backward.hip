@@ -268,7 +268,7 @@ __device__ __forceinline__ void dz_rows(const GemmArgs& a, const GTile& t, int w
 // consecutive vocab positions of each A block, which become 4 bf16 (8 bytes). A group of four A
 // blocks (64 positions = 128 bytes of a dz row) is regrouped to 16 bytes per lane in two steps:
 // v_permlane16_swap exchanges 16-lane rows 1 <-> 0 and 3 <-> 2 between blocks (i, i+1), so that
-// lane 16 g + r holds positions 8 (g >> 1) .. +7 of block i + (g & 1) (likewise P for blocks
+// lane 16 g + r holds positions 8 (g >> 1) .. +7 of block i + (g & 1) (P; likewise Q for blocks
 // i+2, i+3), then the ror8 step above pairs token rows r and r + 8. The epilogues index the
 // accumulators with compile-time constants (static_for): a runtime index would move them to
 // scratch.
