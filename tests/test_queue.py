@@ -1,6 +1,6 @@
-"""Host check of the persistent LM-head kernel's work queues: the kernel's own queue code
-(csrc/rlk_queue.h, compiled for the host) must hand out every (vocab block, row tile) item of a
-launch exactly once, whatever the launch geometry. No GPU is needed.
+"""Host check of the persistent kernels' work queues (the LM-head kernel and the backward GEMMs):
+the kernels' own queue code (csrc/rlk_queue.h, compiled for the host) must hand out every item of
+a launch exactly once, whatever the launch geometry. No GPU is needed.
 
 A dropped item would leave a tile's partials unwritten and a repeated one would only cost time,
 so coverage is what makes a schedule-independent result possible (RL-Kernel v0.1.0 summary,
@@ -61,6 +61,26 @@ def test_workload_launches(checker):
         _launch(600, 65536, 256),               # largest hidden size (bands of 2)
         _launch(257, 256, 1000),                # one row past a row tile
         _launch((1 << 21) + 3, 1024, 1000),     # the 2^21 + 3 row test
+    ])
+
+
+def _gemm(M: int, N: int, batches: int = 1):
+    """(n_vb, n_tt, rb) of a backward GEMM launch: 256 x 256 tiles, the items A tiles x (batch,
+    B tile), one band per batch."""
+    n_mt, n_nt = -(-M // 256), -(-N // 256)
+    return n_mt, n_nt * batches, n_nt
+
+
+def test_backward_gemm_launches(checker):
+    J = 4 * 38016  # Qwen3-8B head: 4 segments of 37984 positions padded to 128
+    _run(checker, [
+        _gemm(J, 4096),            # dz: padded positions x rows
+        _gemm(4096, 4096, 4),      # dh: hidden columns x rows, one batch per segment
+        _gemm(4096, J),            # dW: hidden columns x padded positions
+        _gemm(J // 4, 4096),       # dz of one TP4 shard
+        _gemm(128, 1, 8),          # tiny: 8 segments of one row
+        _gemm(5120, 8192, 4),      # fused-norm head's dh
+        _gemm(300, 77, 2),
     ])
 
 
