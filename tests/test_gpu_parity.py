@@ -62,7 +62,10 @@ SHAPES = [
     (27, 640, 3000, 4, 1.0, True),     # 17..32 rows, H not a multiple of 256 (128-K stages)
     (32, 1024, 151936, 4, 1.0, False), # 32 rows over 4 x 594 tiles (3 items per streaming block)
     (1030, 128, 768, 4, 1.3, True),    # many row tiles, segments of 3 tiles (blocks of 4 with one absent)
-    (1024, 256, 3000, 2, 1.0, True),   # whole row tiles: the queues' last items run as quarters
+    (1024, 256, 3000, 2, 1.0, True),   # whole row tiles: 4 row tiles x 12 vocab blocks
+    (100, 384, 20000, 4, 1.0, False),  # 65-128 rows: 3-tile blocks of 12 waves x 32 rows
+    (160, 256, 20000, 4, 0.7, True),   # 129-192 rows: 12 waves x 48 rows (3 token blocks each)
+    (230, 256, 20000, 2, 1.0, True),   # 193-256 rows: 12 waves x 64 rows, split LDS rings
     (40, 128, 516, 4, 1.0, True),      # segments of 129 = 2 tiles + a 1-column tile
     (70, 128, 160, 8, 1.0, False),     # segments of 20 columns: one partial tile each
     (250, 256, 2500, 1, 1.0, True),    # 40 tiles: two fold groups of 32 and 8
