@@ -48,7 +48,7 @@ CASES = [
     (150, 256, 4000, 4, 1.0, False, {}),                 # 129..192 rows
     (77, 384, 2048, 4, 1.0, True, {}),                   # 65..128 rows, whole tiles only
     (20, 128, 9000, 1, 1.0, True, {}),                   # one segment of 141 tiles: 5 fold groups
-    (512, 256, 5000, 4, 0.7, True, {}),                  # 256-row multiple: quarter items
+    (512, 256, 5000, 4, 0.7, True, {}),                  # whole row tiles (2 x 256)
     (16, 512, 3000, 4, 0.7, True, {}),                   # <= 16 rows: streaming kernel, 256-K stages
     (29, 384, 3000, 2, 1.0, True, {}),                   # 17..32 rows: 2 compute waves, 128-K stages
     (5, 256, 2600, 4, 1.0, False, {}),                   # streaming kernel, one 256-K stage per tile
