@@ -127,23 +127,27 @@ __device__ __forceinline__ uint32_t ror8(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xF, 0xF, false);
 }
 
-// One B1 value.
+// One B1 value before its rounding to bf16.
 template <bool ENTG, bool TEMP, bool PORT>
-__device__ __forceinline__ uint16_t dz_one(float acc, int v, int y, float g, float l, float gh,
-                                           float e, float inv_tau) {
+__device__ __forceinline__ float dz_q(float acc, int v, int y, float g, float l, float gh, float e,
+                                      float inv_tau) {
   const float zp = TEMP ? acc * inv_tau : acc;
   const float p = EXP<PORT>(zp - l);
   const float d = (v == y) ? 1.0f - p : -p;
   float q = g * d;
   if constexpr (ENTG) q = q - gh * (p * ((zp - l) + e));
   if constexpr (TEMP) q = q * inv_tau;
-  // bf16_rne (NaN kept quiet) and the padded-row zero as mask arithmetic: the compiler would
-  // otherwise wrap each element in branches
-  const uint32_t u = __float_as_uint(q);
-  const uint32_t rne = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-  const uint32_t nan = 0u - (uint32_t)((u & 0x7fffffffu) > 0x7f800000u);
-  const uint32_t bits = (rne & ~nan) | (((u >> 16) | 0x40u) & nan);
-  return (uint16_t)(bits & (0u - (uint32_t)(y >= 0)));
+  return q;
+}
+
+// Two values rounded to bf16 (to nearest even, a NaN kept quiet with its top payload bits), as
+// one word: gfx950's v_cvt_pk_bf16_f32, whose results equal that rounding written out in integer
+// arithmetic for every one of the 2^32 fp32 inputs (checked exhaustively on the device).
+__device__ __forceinline__ uint32_t pack_bf16(float x0, float x1) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  const f2 x = {x0, x1};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, b2));
 }
 
 // Staging of one tile: per-lane DMA offsets of stage 0 and the operands' buffer descriptors.
@@ -298,16 +302,16 @@ __device__ __forceinline__ void dz_epilogue(const GemmArgs& a, f32x4 (&acc)[kGVB
         const uint32_t sg = col0 / Lp;
         const uint32_t c0 = col0 - sg * Lp;           // position inside the segment
         const int v0 = (int)(a.v_base + sg * L + c0);  // vocab index of col0 when c0 < L
-        uint16_t b[4];
+        // padding positions and rows without a target give +0
+        float x[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint16_t x = dz_one<ENTG, TEMP, PORT>(acc[i0 + q][j][e], v0 + e, rw.y[j],
-                                                      rw.g[j], rw.l[j], rw.h[j], rw.e[j],
-                                                      a.inv_tau);
-          b[e] = c0 + e < L ? x : (uint16_t)0;
-        }
-        w[q][0] = (uint32_t)b[0] | ((uint32_t)b[1] << 16);
-        w[q][1] = (uint32_t)b[2] | ((uint32_t)b[3] << 16);
+        for (int e = 0; e < 4; ++e)
+          x[e] = c0 + e < L ? dz_q<ENTG, TEMP, PORT>(acc[i0 + q][j][e], v0 + e, rw.y[j], rw.g[j],
+                                                     rw.l[j], rw.h[j], rw.e[j], a.inv_tau)
+                            : 0.0f;
+        const uint32_t ym = 0u - (uint32_t)(rw.y[j] >= 0);
+        w[q][0] = pack_bf16(x[0], x[1]) & ym;
+        w[q][1] = pack_bf16(x[2], x[3]) & ym;
       });
       uint32_t P[4], Q[4];
       {
