@@ -1210,10 +1210,10 @@ hipError_t launch_lmhead(const LmheadArgs& a, int bt, bool ent, hipStream_t s) {
     if (three_tile_blocks(a)) {
       if (a.rows > 192) return launch_deep<3, 4, 4, 3, 3, 2>(a, ent, s);
       // 12 waves (3 per SIMD; 6 waves would load two SIMDs with two waves and two with one):
-      // 48 or 32 rows per wave, W and the hidden rows in one ring of 3 stages
+      // 48, 32 or 16 rows per wave, W and the hidden rows in one ring of 3 (4) stages
       if (a.rows > 128) return launch_deep<3, 4, 3, 3, 3>(a, ent, s);
       if (a.rows > 64) return launch_deep<3, 4, 2, 3, 3>(a, ent, s);
-      return launch_deep<3, 2, 2, 3, 3>(a, ent, s);
+      return launch_deep<3, 4, 1, 4, 3>(a, ent, s);
     }
     bt = a.rows > 128 ? 256 : a.rows > 64 ? 128 : a.rows > 32 ? 64 : 32;
   }
