@@ -130,8 +130,8 @@ struct GemmArgs {
   // OUT
   float* C;
   int64_t ldc;
-  int64_t c_batch;          // C offset per blockIdx.y (one vocab segment per y for dh)
-  int64_t a_batch, b_batch; // A / B offsets per blockIdx.y
+  int64_t c_batch;          // C offset per batch (one vocab segment per batch for dh)
+  int64_t a_batch, b_batch; // A / B offsets per batch
   int32_t accumulate;       // start the chain from C's stored values
   int32_t map_rows;         // OUT rows n are segment-padded vocab rows (skip padding rows)
   int64_t ka_rows, kb_rows; // valid K rows of a K-major A / B
