@@ -650,8 +650,9 @@ __global__ void __launch_bounds__(64 * VW * TW) k_lmhead_deep(const LmheadArgs a
 }
 
 // --------------------------------------------------------------------------------------------
-// K1s: streaming LM-head kernel for launches of at most 256 rows (decode batches). Same MFMA
-// chain (C1), fragment order and per-tile epilogue as k_lmhead, hence the same bits.
+// K1s: streaming LM-head kernel for decode launches of at most 16 rows (32 when H is not a
+// multiple of 256). Same MFMA chain (C1), fragment order and per-tile epilogue as k_lmhead, hence
+// the same bits.
 //
 // A decode launch is bound by the W stream: every W row is used by at most 256 rows. Loads
 // complete in issue order per wave, so a wave that waits for a recent load also waits for every
@@ -856,6 +857,187 @@ __global__ void __launch_bounds__(64 * (CW + NPW)) k_lmhead_stream(const LmheadA
   unroll_seq(seq, [&](auto sc) __attribute__((always_inline)) {
     if (g + decltype(sc)::value < total) step(sc, g + decltype(sc)::value);
   });
+}
+
+// --------------------------------------------------------------------------------------------
+// K1i: LM-head kernel for decode launches of up to 128 rows. Same MFMA chain (C1), fragment order
+// and per-tile epilogue as k_lmhead, hence the same bits.
+//
+// How fast HBM delivers a W stream depends on its order: DMA probes streaming a 311 MB vocab
+// segment from 198 CUs, each owning 3 tiles (192 W rows), reach ~6 TB/s when every request takes
+// 512 contiguous bytes of 64 rows of one tile, but ~4.8-5.1 TB/s when a stage takes 128 (or 256)
+// bytes of all 192 rows at once, which is how k_lmhead_deep stages W. So here a W stage is one
+// tile's 64 rows x 256 K (32 KB), and the block cycles through its NT tiles within each 256-K
+// chunk: stage g holds chunk g / NT of tile g % NT, and a chunk of the hidden rows serves NT
+// consecutive stages. The hidden rows share each CU's memory path with W, and how they are
+// fetched matters as much: the same probes slow from 55 to 77 us (128 rows) when the rows come as
+// MFMA fragments (16 rows x 64 bytes per load) but only to 66 us as whole 128-byte lines.
+//  - NPW producer waves copy W into a ring of NS stages, keep NS-1 in flight and wait, before
+//    each stage's barrier, only for their own copy of that stage;
+//  - CW compute waves own 16 NBW rows each and all NT tiles' columns. Each loads its rows' next
+//    chunk as whole lines into registers a chunk ahead, writes it into its own slice of an LDS
+//    buffer after its last read of the current chunk, and reads its hidden fragments from there
+//    (a wave's slice is only ever touched by that wave: its LDS accesses complete in order, so
+//    no barrier guards it). The compute waves' loads never wait on W (separate counts).
+// One item (NT consecutive tiles of a segment; past a segment's end the rows are clamped and the
+// epilogue skips the missing tiles) per block.
+// --------------------------------------------------------------------------------------------
+template <int CW, int NBW, int NS, int NPW, int NT, bool ENT, bool TEMP, bool PORT>
+__global__ void __launch_bounds__(64 * (CW + NPW)) k_lmhead_il(const LmheadArgs a) {
+  constexpr int SK = 256;                 // K of a stage and of a hidden chunk
+  constexpr int RB = 2 * SK;              // bytes of one staged row (512)
+  constexpr int SW = kVocabTile * RB;     // bytes of one W stage (32 KB)
+  constexpr int DPS = SW / 1024;          // DMA instructions per stage (1 KB each)
+  constexpr int DPW = DPS / NPW;          // ... per producer wave
+  constexpr int KS = SK / 32;             // MFMA K-steps per stage
+  constexpr int RPI = 1024 / RB;          // staged rows per DMA instruction
+  constexpr int BT = 16 * NBW * CW;       // rows of the block
+  constexpr int NL = 8 * NBW;             // line loads per compute wave per chunk (1 KB each)
+  static_assert(NPW * DPW == DPS && NS >= 3 && (NS - 2) * DPW <= 63 && NT >= 1, "stages");
+  static_assert(NS * SW + BT * RB <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_w[NS * SW];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_h[BT * RB];
+  // in both buffers, piece c (16 bytes) of staged row r sits at position c ^ (r & 15): a fragment
+  // read (16 consecutive rows, one piece each) covers the 64 banks evenly
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int H = a.H;
+  const int nc = H / SK;      // K chunks (the launcher checks that SK divides H)
+  const int total = nc * NT;  // stages of the block
+  Tile t;
+  {
+    const int ips = (a.tiles_per_seg + NT - 1) / NT;  // items per segment
+    const int it = (int)blockIdx.x;
+    const int seg = a.seg_begin + it / ips;
+    const int jt = (it % ips) * NT;
+    const int64_t col0 = (int64_t)jt * kVocabTile;
+    t.start = uni64((int64_t)seg * a.seg_len + col0);
+    t.len = uni((int)min((int64_t)NT * kVocabTile, a.seg_len - col0));
+    t.tile0 = uni(seg * a.tiles_per_seg + jt);
+    t.row0 = 0;
+    t.rows = a.rows;
+  }
+
+  if (wave >= CW) {
+    // ---- producer: stage g = (chunk g / NT, tile g % NT) into the ring ----
+    const int p = wave - CW;
+    const uint32_t lbase = (uint32_t)(uintptr_t)lds_w;
+    const i32x4 desc = buffer_desc(a.W + (t.start - a.w_row0) * (int64_t)H, (uint32_t)(t.len * H * 2));
+    int rq[DPW], cq[DPW];  // tile row and logical piece of this lane's 16 bytes, per instruction
+#pragma unroll
+    for (int d = 0; d < DPW; ++d) {
+      const int q = d * NPW + p;  // instruction q fills tile rows RPI q .. RPI q + RPI - 1
+      rq[d] = RPI * q + lane / (RB / 16);
+      cq[d] = (lane % (RB / 16)) ^ (rq[d] & 15);
+    }
+    auto issue = [&](int g) {
+      const int kc = g / NT, u = g % NT;
+      const uint32_t dst = (uint32_t)uni((int)(lbase + (uint32_t)(g % NS) * SW));
+      const uint32_t so = (uint32_t)uni(kc * RB);
+#pragma unroll
+      for (int d = 0; d < DPW; ++d) {
+        const int r = min(kVocabTile * u + rq[d], t.len - 1);
+        dma16_asm(desc, dst + (uint32_t)(d * NPW + p) * 1024u, (uint32_t)(r * H + cq[d] * 8) * 2u, so);
+      }
+    };
+    const int pro = min(NS - 1, total);
+    for (int g = 0; g < pro; ++g) issue(g);
+    for (int g = 0; g < total; ++g) {
+      // stage g has landed (for this wave) once at most the younger stages are in flight
+      wait_vm_n<DPW, NS - 2>(min(NS - 2, total - 1 - g));
+      __asm__ volatile("s_barrier" ::: "memory");
+      // the slot of stage g - 1 is free: every compute wave finished it before this barrier
+      if (g + NS - 1 < total) issue(g + NS - 1);
+    }
+    return;
+  }
+
+  // ---- compute waves ----
+  const int rows = a.rows;
+  const bool has_rows = 16 * NBW * wave < rows;  // uniform: this wave owns a row of the launch
+  const int r0 = 16 * NBW * wave;                // the wave's first row (of the launch and of lds_h)
+  // Line load i of a chunk: rows 8 (i / 4) .. +7 of the wave (lane >> 3 picks the row, clamped
+  // into the launch), bytes 128 (i % 4) + 16 (lane & 7) of the chunk's 512; it lands in lds_h at
+  // the row's position for logical piece 8 (i % 4) + (lane & 7), i.e. 16 B unit
+  // ((lane & 7) ^ (lane >> 3)) + 8 ((i % 4) ^ ((i / 4) & 1)) of the row (r & 15 = 8 ((i / 4) & 1)
+  // + (lane >> 3)).
+  const uint8_t* hbase = (const uint8_t*)a.hidden;
+  uint32_t goff[2 * NBW];  // per 8-row group
+  uint32_t soff[2 * NBW];
+#pragma unroll
+  for (int q = 0; q < 2 * NBW; ++q) {
+    const int lr = r0 + 8 * q + (lane >> 3);
+    goff[q] = (uint32_t)(min(lr, rows - 1) * H) * 2u + 16u * (lane & 7);
+    soff[q] = (uint32_t)lr * RB + (uint32_t)(((lane & 7) ^ (lane >> 3)) << 4);
+  }
+  u32x4 hv[NL];
+  auto load_lines = [&](int kc) __attribute__((always_inline)) {  // chunk kc (mod nc)
+    const uint32_t ko = (uint32_t)(kc % nc) * RB;
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+      hv[i] = *(const u32x4*)(hbase + goff[i / 4] + ko + 128u * (i % 4));
+  };
+  auto store_lines = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+      *(u32x4*)(lds_h + soff[i / 4] + 128u * ((i % 4) ^ ((i / 4) & 1))) = hv[i];
+  };
+  load_lines(0);
+  store_lines();
+  load_lines(1);
+  const int r16 = lane & 15;
+  int loff[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) loff[s] = r16 * RB + (((4 * s + (lane >> 4)) ^ r16) << 4);
+  const uint8_t* hp = lds_h + r0 * RB;  // the wave's rows
+  f32x4 acc[4 * NT][NBW];
+#pragma unroll
+  for (int i = 0; i < 4 * NT; ++i)
+#pragma unroll
+    for (int j = 0; j < NBW; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0f;
+  int ytgt[NBW];
+  load_targets<NBW>(ytgt, a, t, wave, lane);
+
+  int g = 0;
+  for (int kc = 0; kc < nc; ++kc) {
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+      // every LDS read of the previous stage is done before its slot is handed back
+      __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      const uint8_t* sp = lds_w + (g % NS) * SW;
+      // W and hidden fragments one K-step ahead of the MFMAs that use them (a wave without rows
+      // of the launch computes on clamped rows; only its epilogue is skipped)
+      bf16x8 fa[2][4], fb[2][NBW];
+      auto frags = [&](int s, int slot) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fa[slot][i] = *(const bf16x8*)(sp + i * 16 * RB + loff[s]);
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) fb[slot][j] = *(const bf16x8*)(hp + j * 16 * RB + loff[s]);
+      };
+      frags(0, 0);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        if (s + 1 < KS) frags(s + 1, (s + 1) & 1);
+#pragma unroll
+        for (int j = 0; j < NBW; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[4 * u + i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                fa[s & 1][i], fb[s & 1][j], acc[4 * u + i][j], 0, 0, 0);
+      }
+      if (u == NT - 1) {
+        // after the chunk's last reads of the wave's rows: the next chunk replaces them, and
+        // the one after that is fetched (past the last chunk: the first ones again, harmless)
+        store_lines();
+        load_lines(kc + 2);
+      }
+      ++g;
+    }
+  }
+  if (has_rows) tile_epilogue<4 * NT, NBW, ENT, TEMP, PORT>(acc, ytgt, a, t, 0, wave, lane);
 }
 
 // --------------------------------------------------------------------------------------------
@@ -1167,6 +1349,20 @@ static hipError_t launch_stream(const LmheadArgs& a, bool ent, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int CW, int NBW, int NS, int NPW, int NT>
+static hipError_t launch_il(const LmheadArgs& a, bool ent, hipStream_t s) {
+  const int64_t items = (int64_t)a.n_seg * ((a.tiles_per_seg + NT - 1) / NT);
+  if (items == 0 || a.rows == 0) return hipSuccess;
+  if (a.rows > 16 * NBW * CW || a.H % 256 != 0) return hipErrorInvalidValue;
+  if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)items), block(64 * (CW + NPW));
+  with_modes(a, ent, [&](auto e, auto t, auto p) {
+    hipLaunchKernelGGL((k_lmhead_il<CW, NBW, NS, NPW, NT, e.value, t.value, p.value>), grid, block,
+                       0, s, a);
+  });
+  return hipGetLastError();
+}
+
 template <int VW, int TW, int NB16, int NS, int NTPB, int HS = 0>
 static hipError_t launch_deep(const LmheadArgs& a, bool ent, hipStream_t s) {
   constexpr int BT = 16 * NB16 * TW;
@@ -1198,15 +1394,17 @@ static bool three_tile_blocks(const LmheadArgs& a) {
 hipError_t launch_lmhead(const LmheadArgs& a, int bt, bool ent, hipStream_t s) {
   if (bt == 0) {
     if (a.rows > 256) return launch_variant<2, 4, 2>(a, ent, s);
-    // up to 32 rows: the W stream alone bounds the launch (streaming kernel, measured 57 us
-    // per 311 MB vocab segment against 67 us for 3-tile blocks); more rows: 3-tile blocks
-    if (a.rows <= 32) {
-      if (a.H % 256 == 0) {
-        if (a.rows <= 16) return launch_stream<1, 1, 2, 256, 4, 4>(a, ent, s);
-        return launch_stream<2, 1, 2, 256, 4, 4>(a, ent, s);
-      }
-      return launch_stream<2, 1, 3, 128, 8, 2>(a, ent, s);
+    // up to 128 rows: W streamed tile by tile in 512-byte rows, the hidden rows fetched as
+    // whole lines (k_lmhead_il; per 311 MB vocab segment 59-61 us up to 64 rows and 66-68 us up
+    // to 128, against 64-72 us for the streaming kernel and 3-tile blocks); up to 16 rows the
+    // streaming kernel
+    if (a.rows <= 128 && a.H % 256 == 0) {
+      if (a.rows <= 16) return launch_stream<1, 1, 2, 256, 4, 4>(a, ent, s);
+      if (a.rows <= 32) return launch_il<2, 1, 4, 4, 3>(a, ent, s);
+      if (a.rows <= 64) return launch_il<4, 1, 4, 4, 3>(a, ent, s);
+      return launch_il<8, 1, 3, 4, 3>(a, ent, s);
     }
+    if (a.rows <= 32) return launch_stream<2, 1, 3, 128, 8, 2>(a, ent, s);
     if (three_tile_blocks(a)) {
       if (a.rows > 192) return launch_deep<3, 4, 4, 3, 3, 2>(a, ent, s);
       // 12 waves (3 per SIMD; 6 waves would load two SIMDs with two waves and two with one):
