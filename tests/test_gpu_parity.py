@@ -60,7 +60,11 @@ SHAPES = [
     (1, 128, 4000, 8, 1.0, True),      # a single row, 8 segments of 500 = 7 tiles + 52
     (16, 256, 5000, 2, 0.7, True),     # <= 16 rows (streaming kernel), temperature
     (27, 640, 3000, 4, 1.0, True),     # 17..32 rows, H not a multiple of 256 (128-K stages)
-    (32, 1024, 151936, 4, 1.0, False), # 32 rows over 4 x 594 tiles (3 items per streaming block)
+    (32, 1024, 151936, 4, 1.0, False), # 17..32 rows over 4 x 594 tiles: 3-tile items, W by whole tile rows
+    (17, 256, 4000, 4, 1.0, True),     # 17 rows: one of 2 compute waves has a single row
+    (50, 512, 10000, 4, 0.7, True),    # 33..64 rows: 4 compute waves, temperature
+    (128, 256, 8000, 2, 1.0, False),   # 65..128 rows: 8 compute waves, segments of 62.5 tiles
+    (100, 768, 2500, 1, 0.7, True),    # 3 K chunks of 256, one segment: last item 1 partial tile
     (1030, 128, 768, 4, 1.3, True),    # many row tiles, segments of 3 tiles (blocks of 4 with one absent)
     (1024, 256, 3000, 2, 1.0, True),   # whole row tiles: 4 row tiles x 12 vocab blocks
     (100, 384, 20000, 4, 1.0, False),  # 65-128 rows: 3-tile blocks of 12 waves x 32 rows

@@ -53,6 +53,9 @@ CASES = [
     (29, 384, 3000, 2, 1.0, True, {}),                   # 17..32 rows: 2 compute waves, 128-K stages
     (5, 256, 2600, 4, 1.0, False, {}),                   # streaming kernel, one 256-K stage per tile
     (9, 256, 5600, 8, 0.7, True, {}),                    # 8 segments of 700
+    (29, 512, 3000, 2, 0.7, True, {}),                   # 17..32 rows: interleaved 3-tile kernel
+    (60, 256, 5000, 4, 1.0, True, {}),                   # 33..64 rows, last item of 2 tiles
+    (100, 768, 2500, 1, 0.7, False, {}),                 # 65..128 rows, 3 K chunks
     (300, 256, 5000, 4, 1.0, True, {"token_tile": 32}),
     (300, 256, 5000, 4, 1.0, True, {"token_tile": 64}),
     (300, 256, 5000, 4, 1.0, True, {"token_tile": 128}),
