@@ -532,6 +532,24 @@ def reference_logp(np, name: str):
     return np.load(f, allow_pickle=False)[0] if os.path.exists(f) else None
 
 
+def d6_record(rlk, np, torch, case: str, contract_id: str, logp, y, ref, ms: float,
+              mismatch, mismatch_against: str) -> dict:
+    """A report record (the pages' field subset: requested case, backend and fingerprints,
+    fallbacks, active rows, mismatch_count, logprob_abs_diff_* against the oracle's stored
+    outputs of every active row, wall time, tokens/s, peak memory) for one measured case."""
+    act = y >= 0
+    n = int(act.sum())
+    rec = {"requested_case": case, "backend": "rlk_logprob (HIP, gfx950)", "contract_id": contract_id,
+           "build_fingerprint": rlk.rlk_build_fingerprint(),
+           "hardware_fingerprint": hardware_fingerprint(torch), "fallbacks": [],
+           "active_token_count": n, "mismatch_count": mismatch, "mismatch_against": mismatch_against,
+           "wall_ms_per_step": ms, "tokens_per_second": n / (ms * 1e-3),
+           "peak_memory_bytes": int(torch.cuda.max_memory_allocated())}
+    if ref is not None:
+        rec["vs_oracle"] = diff_stats(logp[act], ref[act])
+    return rec
+
+
 def long_grpo(rlk, datagen, np, torch, Wd) -> dict:
     """The long GRPO batch (8 samples x 6912 tokens, 553 trailing pads, the Qwen3-8B head's W): one
     pass and 8192-row chunks, throughput over the active rows, and the chunked run's bit
@@ -560,6 +578,12 @@ def long_grpo(rlk, datagen, np, torch, Wd) -> dict:
                          fl / (r["lmhead_ms_per_step"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
     out["mismatch_count_chunks_vs_one_pass"] = int(np.count_nonzero(
         one["_logp"].view(np.uint32) != ch["_logp"].view(np.uint32)))
+    ref = reference_logp(np, w.name)
+    out["report"] = d6_record(rlk, np, torch, "long_grpo (8192-row chunks)", lp.contract_id,
+                              ch["_logp"], y, ref, ch["ms_per_step"],
+                              out["mismatch_count_chunks_vs_one_pass"], "one pass")
+    if ref is not None:
+        out["report"]["vs_oracle_one_pass"] = diff_stats(one["_logp"][y >= 0], ref[y >= 0])
     del hd, yd, lp
     return out
 
@@ -612,6 +636,12 @@ def rollout(rlk, datagen, np, hd, Wd, yd, w, ref_logp, steps: int = 3, warmup: i
     if ref_logp is not None:
         res["mismatch_count_vs_one_pass"] = int(np.count_nonzero(
             r["_logp"].view(np.uint32) != ref_logp.view(np.uint32)))
+    import torch
+
+    res["report"] = d6_record(rlk, np, torch, "tp4_shards (decode batches x 4 vocab shards)",
+                              lp.contract_id, r["_logp"], yd.cpu().numpy(),
+                              reference_logp(np, w.name), r["ms_per_step"],
+                              res.get("mismatch_count_vs_one_pass"), "one pass")
     return res
 
 
@@ -668,6 +698,15 @@ def extras(rlk, datagen, np, torch, hd, Wd, yd, w, ref_logp) -> dict:
         "tokens_per_s": wn.T / (r["ms_per_step"] * 1e-3),
         "lmhead_ms": r["lmhead_ms_per_step"],
         "lmhead_frac_of_bf16_peak": fl / (r["lmhead_ms_per_step"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    log("norm_head in decode batches x 4 shards (layout check)")
+    rd = time_layout(rlk, lpn, xd, Wnd, ynd, gd, wn.T, 1, 0,
+                     dict(batch_sizes=datagen.decode_layout(wn.T), vocab_shards=4))
+    mm = int(np.count_nonzero(rd["_logp"].view(np.uint32) != r["_logp"].view(np.uint32)))
+    out["norm_head_one_pass"]["mismatch_count_decode_x4_vs_one_pass"] = mm
+    out["norm_head_one_pass"]["report"] = d6_record(
+        rlk, np, torch, "norm_head (RMSNorm + temperature + entropy, one pass)", lpn.contract_id,
+        r["_logp"], yn, reference_logp(np, wn.name), r["ms_per_step"], mm,
+        "decode batches x 4 vocab shards")
     del xd, Wnd, lpn
     return out
 
@@ -853,6 +892,11 @@ def main() -> int:
     if "ablation_matrix" in result.get("extras", {}):
         rep["ablation_matrix"] = result["extras"]["ablation_matrix"]["cells"]
     result["report"] = rep
+    # one record per measured configuration (this run's case first, then the extras')
+    ex = result.get("extras", {})
+    result["reports"] = [rep] + [
+        x["report"] for x in (ex.get("tp4_decode_x4_shards"), ex.get("long_grpo"),
+                              ex.get("norm_head_one_pass")) if x and "report" in x]
     print(json.dumps(result), flush=True)
     del keep
     return 0
