@@ -16,7 +16,8 @@ from tests.helpers import assert_bitwise, dev_bits, dev_i32, host, say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("layout", [dict(), dict(batch_sizes=[1, 255, 0, 40, 404], vocab_shards=4)])
+@pytest.mark.parametrize(
+    "layout", [dict(), dict(batch_sizes=[1, 255, 0, 20, 40, 100, 284], vocab_shards=4)])
 def test_forward_graph_replays_equal_eager(rlk, layout):
     import torch
 
